@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MLA-over-NVFP4 hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3|c2] [--splits S] [--no-cpu-baseline]
+
+One step = one decode step of the whole path for every request of the
+workload: quantized write of each request's newest KV row, dedup compaction of
+the requests' top-k lists, sparse MLA decode over the compacted lists
+(per-split kernel), and the (o, lse) merge.  Inputs (4.6 GB pool, page table,
+lists, queries) are resident in HBM before timing; 8 rotating list/query sets
+keep the gathered rows from being served out of the 256 MB Infinity Cache.
+
+Prints one JSON line: decode tokens/s (value), the roofline of the dominant
+kernel (the per-split decode kernel, timed with HIP events on the stream it
+runs on), prefill MFMA utilisation, and the CPU oracle on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+N_SETS = 8                     # rotating list/query sets
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's automatic choice")
+    ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (a known-size kernel for counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- setup
+def build_decode_workload(spec, dev, n_sets=N_SETS):
+    """Device pool (all slots quantized by kv4_quant_write from device-drawn
+    fp32 rows), page table, rotating lists / queries / new rows."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+
+    pool = torch.empty((spec.n_slots, 352), dtype=torch.uint8, device=dev)
+    n_chunks = -(-spec.n_slots // W.KV_CHUNK)
+    for c in range(n_chunks):
+        x = W.kv_chunk_device(spec, c, dev)
+        lo = c * W.KV_CHUNK
+        slots = torch.arange(lo, lo + x.shape[0], dtype=torch.int32, device=dev)
+        kv4.quant_write(x, slots, pool)
+        del x
+    pt_h = W.page_table(spec)
+    sets = []
+    for i in range(n_sets):
+        s = W.scaled(spec, seed=spec.seed + 17 * i) if i else spec
+        topk_h = W.topk_lists(s)
+        q = W.queries(s)
+        g = np.random.default_rng([spec.seed, 99, i])
+        new_rows = g.standard_normal((spec.n_req, 576), dtype=np.float32)
+        sets.append(dict(topk_h=topk_h, topk=torch.from_numpy(topk_h).to(dev), q=q.to(dev),
+                         new_rows=torch.from_numpy(new_rows).to(dev)))
+    last = spec.ctx - 1
+    new_slots = (pt_h[:, last >> 6].astype(np.int64) * 64 + (last & 63)).astype(np.int32)
+    torch.cuda.synchronize(dev)
+    return dict(pool=pool, pt_h=pt_h, pt=torch.from_numpy(pt_h).to(dev), sets=sets,
+                new_slots=torch.from_numpy(new_slots).to(dev), new_slots_h=new_slots)
+
+
+def gathered_rows_host(spec, pt_h, topk_h, dev):
+    """fp32 originals of the rows the lists select, regenerated from the same
+    device draws (for the oracle); returns (unique slots, rows [n, 576])."""
+    import torch
+    import workloads as W
+    slots = (pt_h[np.arange(topk_h.shape[0])[:, None], topk_h >> 6].astype(np.int64) * 64 + (topk_h & 63))
+    uniq = np.unique(slots)
+    rows = np.empty((uniq.size, 576), dtype=np.float32)
+    chunk_of = uniq // W.KV_CHUNK
+    for c in np.unique(chunk_of):
+        sel = np.nonzero(chunk_of == c)[0]
+        x = W.kv_chunk_device(spec, int(c), dev)
+        idx = torch.from_numpy(uniq[sel] - int(c) * W.KV_CHUNK).to(dev)
+        rows[sel] = x.index_select(0, idx).cpu().numpy()
+        del x
+    return uniq, rows, slots
+
+
+# ---------------------------------------------------------- measurement
+def algorithmic_decode_bytes(n_req, n_heads, k, q_bytes=2):
+    """Per launch: each request's k selected rows (352 B), k list entries and
+    k page-table entries (4 B each), its queries (n_heads x 576 x q_bytes) and
+    its output (n_heads x 512 fp32 + n_heads lse)."""
+    per_req = k * 352 + k * 4 * 2 + n_heads * 576 * q_bytes + n_heads * (512 + 1) * 4
+    return per_req * n_req
+
+
+def prefill_flops(n_rows, n_heads, k):
+    """Scores over 576 dims and P.V over 512 dims, 2 flops per multiply-add."""
+    return 2.0 * n_rows * n_heads * k * (576 + 512)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_kv_cache_kv4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter summaries, or None if absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, "sparse_mla_decode_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def run_cpu_baseline(spec, wl, dev):
+    """The oracle, as it is, on the host cores: the same decode step (write
+    the requests' new rows, dedup their lists, attention) for every request
+    of one rotating set, over a host pool of the selected rows that the
+    oracle quantized itself (untimed setup)."""
+    import oracle
+    st = wl["sets"][0]
+    uniq, rows, slots = gathered_rows_host(spec, wl["pt_h"], st["topk_h"], dev)
+    pool_h = np.zeros((uniq.size + spec.n_req, 352), dtype=np.uint8)
+    oracle.quant_write(rows, np.arange(uniq.size, dtype=np.int32), pool_h)
+    compact = np.searchsorted(uniq, slots).astype(np.int32)
+    q = st["q"].float().cpu().numpy()
+    new_rows = st["new_rows"].cpu().numpy()
+    new_slots = np.arange(uniq.size, uniq.size + spec.n_req, dtype=np.int32)
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    oracle.quant_write(new_rows, new_slots, pool_h)
+    lists, _ = oracle.dedup_compact(compact)
+    oracle.sparse_mla(q, pool_h, lists, spec.sm_scale)
+    dt = time.perf_counter() - t0
+    return {"value": spec.n_req / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "one full decode step of %s: %d requests (write %d new rows, dedup %d lists of %d, "
+                      "attention %d heads x %d keys each), host pool of the %d selected rows; %.2f s wall on %d "
+                      "threads" % (spec.name, spec.n_req, spec.n_req, spec.n_req, spec.k, spec.n_heads, spec.k,
+                                   uniq.size, dt, threads)}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.C3 if args.workload == "c3" else W.C2
+    print("[bench] building %s pool: %d slots (%.2f GB)" % (spec.name, spec.n_slots, spec.n_slots * 352 / 1e9),
+          file=sys.stderr, flush=True)
+    wl = build_decode_workload(spec, dev)
+    pool, pt, sets = wl["pool"], wl["pt"], wl["sets"]
+    H, R, K = spec.n_heads, spec.n_req, spec.k
+    S = args.splits or kv4.sparse_mla_decode_splits(sets[0]["q"], pool, sets[0]["topk"], page_table=pt)
+    part_o = torch.empty((S, R, H, 512), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((S, R, H), dtype=torch.float32, device=dev)
+    out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    lists = torch.empty((R, K), dtype=torch.int32, device=dev)
+    counts = torch.empty((R,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        st = sets[i % len(sets)]
+        kv4.quant_write(st["new_rows"], wl["new_slots"], pool)
+        kv4.dedup_compact(st["topk"], out_idx=lists, out_count=counts)
+        if ev is not None:
+            ev[0].record(stream)
+        if S > 1:
+            kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt,
+                                          part_o=part_o, part_lse=part_lse)
+            if ev is not None:
+                ev[1].record(stream)
+            kv4.merge_states(part_o, part_lse, out=out, lse=lse)
+        else:
+            kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=1, out=out, lse=lse)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print("[bench] timing %d steps (splits=%d)" % (args.steps, S), file=sys.stderr, flush=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize(dev)
+
+    algo = algorithmic_decode_bytes(R, H, K)
+    achieved = algo / (split_ms * 1e-3) / 1e9
+    decode_flops = prefill_flops(R, H, K)
+    result = {
+        "metric": "sparse-MLA decode tokens/s + achieved HBM GB/s at top-k 2048; prefill MFMA %",
+        "value": round(R * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": R, "context_tokens": spec.ctx, "heads": H, "topk": K,
+                   "page_size": 64, "pool_rows": spec.n_slots, "pool_gb": round(spec.n_slots * 352 / 1e9, 3),
+                   "q_dtype": spec.q_dtype, "splits": S, "rotating_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
+                     "kernel": "sparse_mla_kernel (per-split decode)", "avg_launch_ms": round(split_ms, 5),
+                     "algorithmic_bytes": algo,
+                     "mfma_tflops": round(decode_flops / (split_ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(decode_flops / (split_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "merge_avg_launch_ms": round(merge_ms, 5),
+        "decode_gbs_incl_merge": round(algo / ((split_ms + merge_ms) * 1e-3) / 1e9, 1),
+    }
+
+    if not args.no_prefill:
+        del part_o
+        result["prefill"] = run_prefill(args, dev)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = run_cpu_baseline(spec, wl, dev)
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(args, dev):
+    """Sparse MLA prefill over the 65,536-token context (4096 queries x 64 heads
+    x top-2048): MFMA utilisation against the dense fp16 peak."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+    spec = W.C5
+    print("[bench] prefill %s" % spec.name, file=sys.stderr, flush=True)
+    kv = torch.from_numpy(W.kv_rows_host(spec, 0, spec.n_slots)).to(dev)
+    pool = torch.empty((spec.n_slots, 352), dtype=torch.uint8, device=dev)
+    kv4.quant_write(kv, torch.arange(spec.n_slots, dtype=torch.int32, device=dev), pool)
+    del kv
+    q = W.queries(spec).to(dev)
+    topk = torch.from_numpy(W.topk_lists(spec)).to(dev)
+    pt = torch.from_numpy(W.page_table(spec)).to(dev)
+    rr = torch.from_numpy(W.row_req(spec)).to(dev)
+    out = torch.empty((spec.rows, spec.n_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((spec.rows, spec.n_heads), dtype=torch.float32, device=dev)
+    kv4.sparse_mla_prefill(q, pool, topk, spec.sm_scale, page_table=pt, row_req=rr, out=out, lse=lse)
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ms = []
+    for _ in range(args.prefill_iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kv4.sparse_mla_prefill(q, pool, topk, spec.sm_scale, page_table=pt, row_req=rr, out=out, lse=lse)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms.append(e0.elapsed_time(e1))
+    t = float(np.median(ms))
+    fl = prefill_flops(spec.rows, spec.n_heads, spec.k)
+    tf = fl / (t * 1e-3) / 1e12
+    return {"workload": spec.name, "query_rows": spec.rows, "heads": spec.n_heads, "topk": spec.k,
+            "context_tokens": spec.ctx, "ms": round(t, 4), "tflops": round(tf, 2),
+            "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "query_tokens_per_s": round(spec.rows / (t * 1e-3), 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stdout (flushed) before it touches the device, so
+    a run that ends abruptly still says which case was running."""
+    if "gpu" in request.node.keywords:
+        import sys as _sys
+        _sys.stdout.write("\n[gpu case] %s\n" % request.node.nodeid)
+        _sys.stdout.flush()
+    yield

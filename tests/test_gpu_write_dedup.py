@@ -1,0 +1,160 @@
+"""GPU parity of the quantized row write and dedup compaction: bit-exact
+against the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_kv4_amd as kv4
+import oracle
+import workloads as W
+from gpu_harness import DEV, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _write_both(kv, slots, n_slots, sentinel=0xA5, stride=None):
+    pool_h = np.full((n_slots, 352), sentinel, np.uint8)
+    err_h = oracle.quant_write(kv, slots, pool_h)
+    pool_d = torch.full((n_slots, 352), sentinel, dtype=torch.uint8, device=DEV)
+    err_d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv_d = to_dev(kv)
+    if stride is not None:
+        wide = torch.zeros((kv.shape[0], stride), dtype=torch.float32, device=DEV)
+        wide[:, :576] = kv_d
+        kv_d = wide[:, :576]
+    kv4.quant_write(kv_d, to_dev(slots), pool_d, err_d)
+    torch.cuda.synchronize()
+    return pool_d.cpu().numpy(), pool_h, int(err_d.item()), err_h
+
+
+def _assert_same_bytes(got, want):
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, "rows differ: %s; first row bytes differ at %s" % (
+        bad[:8].tolist(), np.nonzero(got[bad[0]] != want[bad[0]])[0][:16].tolist())
+
+
+def test_write_c4_full_size_bit_exact():
+    spec = W.C4
+    kv, slots = W.write_tokens(spec), W.write_slots(spec)
+    got, want, e_d, e_h = _write_both(kv, slots, spec.n_slots)
+    _assert_same_bytes(got, want)
+    assert e_d == e_h == 0
+    untouched = np.setdiff1d(np.arange(spec.n_slots), slots)
+    assert (got[untouched] == 0xA5).all()
+
+
+def _adversarial_rows():
+    g = np.random.default_rng(99)
+    rows = []
+    z = np.zeros(576, np.float32)
+    rows.append(z.copy())                                           # all zero
+    rows.append(-z)                                                 # all -0.0
+    rows.append(np.full(576, 1e-30, np.float32))                    # below every scale
+    rows.append(np.full(576, -1e-40, np.float32))                   # fp32 subnormal
+    rows.append(np.full(576, 3e38, np.float32) * g.choice([-1, 1], 576))   # saturation
+    rows.append(np.float32(np.linspace(-1e5, 1e5, 576)))
+    r = g.standard_normal(576).astype(np.float32)
+    r[::7] = 0
+    rows.append(r)
+    # E4M3 scale midpoints (amax = 6 x midpoint, +-2 ulps) in every block
+    v = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)
+    base = (mids * np.float32(6.0)).astype(np.float32).view(np.int32)
+    amax = np.concatenate([(base + k).view(np.float32) for k in range(-2, 3)])
+    for i in range(0, amax.size, 32):
+        r = (g.standard_normal(576) * 0.1).astype(np.float32)
+        a = amax[i:i + 32]
+        for b in range(a.size):
+            r[16 * b:16 * b + 16] *= a[b]
+            r[16 * b + (b % 16)] = a[b] * (1 if b % 2 else -1)
+        r[512:] = np.resize(mids, 64) * g.choice([-1, 1], 64)            # rope at E4M3 midpoints
+        rows.append(r.astype(np.float32))
+    # E2M1 ties: amax = 6d exactly, other entries at d * {0.25, 0.75, ..., 5} (+- ulps)
+    ties = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for k in (-1, 0, 1):
+        r = np.zeros(576, np.float32)
+        for b in range(32):
+            d = np.float32(oracle.e4m3_value(int(g.integers(1, 0x7F))))
+            r[16 * b] = np.float32(6) * d
+            t = (ties * d).astype(np.float32).view(np.int32) + k
+            r[16 * b + 1:16 * b + 8] = t.view(np.float32) * g.choice([-1, 1], 7)
+            r[16 * b + 8:16 * b + 16] = g.uniform(-6, 6, 8).astype(np.float32) * d
+        rows.append(r)
+    return np.stack(rows).astype(np.float32)
+
+
+def test_write_adversarial_rows_bit_exact():
+    kv = _adversarial_rows()
+    n = kv.shape[0]
+    slots = np.arange(n, dtype=np.int32)[::-1].copy()
+    got, want, e_d, e_h = _write_both(kv, slots, n + 3)
+    _assert_same_bytes(got, want)
+    assert e_d == e_h == 0
+
+
+def test_write_pads_out_of_range_and_strided_rows():
+    g = np.random.default_rng(5)
+    kv = (g.standard_normal((70, 576)) * 3).astype(np.float32)
+    slots = g.permutation(100)[:70].astype(np.int32)
+    slots[3] = -1
+    slots[10] = -100
+    slots[20] = 100            # == n_slots: out of range, flagged
+    slots[21] = 1 << 30
+    got, want, e_d, e_h = _write_both(kv, slots, 100, stride=640)
+    _assert_same_bytes(got, want)
+    assert e_d == e_h == kv4.ERRBIT_SLOT
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023])
+def test_write_ragged_token_counts(n):
+    g = np.random.default_rng(n)
+    kv = g.standard_normal((n, 576)).astype(np.float32)
+    slots = g.permutation(2 * n + 1)[:n].astype(np.int32)
+    got, want, e_d, e_h = _write_both(kv, slots, 2 * n + 1)
+    _assert_same_bytes(got, want)
+
+
+def _dedup_both(idx, k=None):
+    out_h, cnt_h = oracle.dedup_compact(idx[:, :k] if k is not None else idx)
+    out_d, cnt_d = kv4.dedup_compact(to_dev(idx), k=k)
+    torch.cuda.synchronize()
+    return out_d.cpu().numpy(), cnt_d.cpu().numpy(), out_h, cnt_h
+
+
+def test_dedup_c4_full_size_bit_exact():
+    idx = W.dup_lists(W.C4)
+    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx)
+    assert (cnt_d == cnt_h).all() and (cnt_h == W.C4.n_distinct).all()
+    assert (out_d == out_h).all()
+
+
+@pytest.mark.parametrize("k", [1, 2, 5, 64, 255, 256, 257, 511, 512, 1000, 2048, 2051, 3000, 4096])
+def test_dedup_lengths_and_edge_lists(k):
+    g = np.random.default_rng(k)
+    L = 37
+    idx = g.integers(-4, max(3, k // 2), size=(L, k)).astype(np.int32)
+    idx[0] = -1                                       # all padding
+    idx[1] = 7                                        # one value
+    idx[2] = np.arange(k, dtype=np.int32)             # all distinct
+    idx[3] = g.integers(0, 2**31 - 1, size=k)         # large values
+    idx[4, ::2] = 2**31 - 1
+    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx)
+    assert (cnt_d == cnt_h).all()
+    assert (out_d == out_h).all()
+
+
+def test_dedup_strided_rows_and_prefix_k():
+    g = np.random.default_rng(3)
+    idx = g.integers(-2, 300, size=(50, 1000)).astype(np.int32)
+    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx, k=700)      # row stride 1000, k 700
+    assert (cnt_d == cnt_h).all() and (out_d == out_h).all()
+
+
+def test_dedup_empty_calls():
+    idx = torch.zeros((0, 16), dtype=torch.int32, device=DEV)
+    out, cnt = kv4.dedup_compact(idx)
+    assert out.shape == (0, 16)
+    idx = torch.zeros((5, 0), dtype=torch.int32, device=DEV)
+    out, cnt = kv4.dedup_compact(idx)
+    torch.cuda.synchronize()
+    assert (cnt.cpu() == 0).all()
