@@ -3,24 +3,37 @@
 // README "60+ inference optimizations & kernels": section "4-bit KV cache"
 // (kv4mla dequantizes the 4-bit rows on chip instead of into an FP8 scratch
 // copy), section "AMD MI355X" (hand-written HIP sparse MLA decode whose K tile
-// in LDS is also the PV operand; split-K decode), "Parallelism and
-// disaggregation" (per-part (o, lse) and a merge).  sgl-amd-mono GLM-5.3 PR,
-// "Modifications": 64-token page table and its stride as launch arguments;
-// one split task serves 16 heads so each key row is gathered once per task.
+// in LDS is also the PV operand through a transposing LDS read; split-K
+// decode), "Parallelism and disaggregation" (per-part (o, lse) and a merge).
+// sgl-amd-mono GLM-5.3 PR, "Modifications": 64-token page table and its stride
+// as launch arguments; a split task serves many heads so each key row is
+// gathered once per task.
 //
-// Workgroup = 4 wavefronts = (query row r, split s, chunk of up to 64 heads).
-// Wavefront w owns 16 heads.  Per tile of 32 list entries:
+// Workgroup = 4 wavefronts = (query row r, split s, chunk of up to 64 heads),
+// one per SIMD with the whole register file (queries and accumulators stay in
+// registers).  Wavefront w = (head group hg = w / 2 of 32 heads, half h = w %
+// 2).  Per tile of 32 list entries:
 //   1. the entries' pool slots (translated once per chunk of 2048 entries and
-//      kept in LDS) name 32 rows; the 256 lanes gather them straight from HBM
-//      (lane = row pair x 16-byte code chunk), one tile ahead of the math;
-//   2. the lanes dequantize codes x block scale and rope to fp16 (every such
-//      product is exact in fp16) into two LDS layouts: K[32 rows][576] for the
-//      scores and V^T[512 dims][32 rows] for P.V;
-//   3. each wavefront computes S^T[32 rows x 16 heads] = K Q^T with
-//      v_mfma_f32_16x16x32_f16 (Q in registers, pre-scaled per head by a power
-//      of two so bf16/fp32 queries fit fp16 exactly), an online softmax in
-//      base 2 with lazy rescaling, and O^T[512 x 16] += V^T P^T with the same
-//      MFMA, P staying in the registers the scores came out in.
+//      kept in LDS) name 32 rows; lane t gathers row t % 32, bytes of part
+//      t / 32 (64 latent dims, their 4 scales, 8 rope dims) straight from HBM,
+//      two tiles ahead of the math;
+//   2. the lanes dequantize with gfx950's FP4/FP8 -> fp16 conversions at scale
+//      1 and one packed multiply by the E4M3 block scale (every product is exact
+//      in fp16) into a row-major K tile [32 rows][576] in LDS, double-buffered
+//      so this overlaps the previous tile's scores;
+//   3. wavefront (hg, h) computes the partial scores S^T[32 rows x 32 heads]
+//      over dims 288h..288h+287 with v_mfma_f32_32x32x16_f16 (queries in
+//      registers, pre-scaled per head by a power of two so they are exact in
+//      fp16), swaps partials with its partner through LDS, and accumulates
+//      O^T[256 dims x 32 heads] for latent dims 256h..256h+255 with the same
+//      MFMA from P = 2^(s - m_ref), where m_ref is the head's largest score in
+//      the first tile that has a valid entry (so the accumulators are never
+//      rescaled).  If a later score exceeds m_ref + 15 (P could overflow fp16)
+//      the workgroup runs the list again with m_ref = the exact maximum seen,
+//      which the first pass tracked.  P^T comes
+//      straight from the score registers and V^T from the K tile through
+//      ds_read_b64_tr_b16, which hands each lane a column of a row-major 4x16
+//      block.
 // The per-split result is written normalised with its lse; a split count of 1
 // writes the final output.
 #include "kv4_device.h"
@@ -29,41 +42,102 @@
 namespace kv4 {
 
 constexpr int kTile = 32;                              // list entries per tile
-constexpr int kKPitchHalf = 584;                       // 576 + 8 pad: conflict-free 16-byte reads
-constexpr int kKPitchDw = kKPitchHalf / 2;
-constexpr int kKTileDw = kTile * kKPitchDw;            // 9344 dwords
-constexpr int kVtPitchDw = 16;                         // 32 rows of fp16 per latent dim, swizzled
-constexpr int kVtDw = kLatent * kVtPitchDw;            // 8192 dwords
+constexpr int kKChunks = 80;                           // 16-byte chunks per K-tile row (72 used)
+constexpr int kKRowBytes = kKChunks * 16;
+constexpr int kKTileBytes = kTile * kKRowBytes;        // 40960
+constexpr int kXBytes = 4 * 64 * 16 * 4 + 16;          // partial scores: 4 wavefronts x 64 lanes x 16, + a flag
 constexpr int kSlotCap = 2048;                         // entries translated per chunk
-constexpr int kLdsDw = kKTileDw + kVtDw + kSlotCap;    // 78336 bytes
-constexpr float kRescaleSlack = 8.0f;                  // log2 units the running max may lag
+constexpr int kLdsBytes = 2 * kKTileBytes + kXBytes + kSlotCap * 4;   // 106496
+constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
 
-// V^T row layout: the 32 rows of a tile sit in the order the score
-// accumulator hands them to each lane group g: positions 8g..8g+3 hold rows
-// 4g..4g+3 and 8g+4..8g+7 hold rows 16+4g..16+4g+3.  Rows 2p and 2p+1 share a
-// dword; vt_pair_dw(p) is that dword.  The dword index is XOR-swizzled by
-// latent dim so 16-byte reads of eight consecutive dims hit distinct banks.
-__device__ __forceinline__ int vt_pair_dw(int p) { return 4 * ((p & 7) >> 1) + 2 * (p >> 3) + (p & 1); }
-__device__ __forceinline__ int vt_swz(int d) { return 4 * ((d >> 1) & 3); }
-__device__ __forceinline__ int vt_addr(int d, int dw) { return d * kVtPitchDw + (dw ^ vt_swz(d)); }
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ floatx4_t mfma16(half8_t a, half8_t b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// K-tile layout: row r starts at r * 1280 + 16 * krot(r) bytes (chunks of 16
+// bytes, 72 used, up to 7 chunks of shift).  krot maps eight consecutive rows
+// onto eight distinct 16-byte bank groups, so the score operand reads (one
+// chunk of rows r..r+7) are conflict-free, and rows 4g..4g+3 start 32 bytes
+// apart modulo 128, so the transposing reads (32 bytes of each of 4 rows) are
+// too.  Every address is a per-lane base plus a compile-time offset.
+__device__ __forceinline__ int krot(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+__device__ __forceinline__ int krow(int r) { return r * kKRowBytes + 16 * krot(r); }
+
+__device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ short4_t lds_read_tr16(const uint8_t *lds_base, int byte_off) {
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_short4 *)((__attribute__((address_space(3))) uint8_t *)lds_base + byte_off));
+}
+
+// One lane's share of a tile's rows: row t % 32, part t / 32 (latent dims
+// 64 part .. +63 as 32 code bytes, their 4 block scales, rope dims 8 part .. +7).
+struct RowPart {
+    u32x4_t c0, c1;
+    uint32_t sc;
+    u32x2_t rp;
+    bool valid;
+};
+
+// A skipped entry reads row 0 (the pool has at least one row whenever a slot
+// can be valid) and is zeroed by dequant_part: scale and rope bytes become 0.
+__device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, int32_t slot, int gp, RowPart &R) {
+    R.valid = slot >= 0;
+    const uint8_t *row = pool + (int64_t)(R.valid ? slot : 0) * kRowBytes;
+    R.c0 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp);
+    R.c1 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp + 16);
+    R.sc = *reinterpret_cast<const uint32_t *>(row + kScaleOff + 4 * gp);
+    R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
+}
+
+__device__ __forceinline__ void dequant_part(uint8_t *ktile, int gr, int gp, const RowPart &R) {
+    const uint32_t sc = R.valid ? R.sc : 0u;
+    const u32x2_t rp = R.valid ? R.rp : u32x2_t{0, 0};
+    const half2_t d0 = block_scale_half(sc & 0xFFu), d1 = block_scale_half((sc >> 8) & 0xFFu);
+    const half2_t d2 = block_scale_half((sc >> 16) & 0xFFu), d3 = block_scale_half(sc >> 24);
+    uint8_t *kr = ktile + krow(gr) + 128 * gp;
+    uint32_t v[4];
+    e2m1x8_to_half_cvt(R.c0[0], d0, v);
+    *reinterpret_cast<u32x4_t *>(kr + 0) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c0[1], d0, v);
+    *reinterpret_cast<u32x4_t *>(kr + 16) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c0[2], d1, v);
+    *reinterpret_cast<u32x4_t *>(kr + 32) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c0[3], d1, v);
+    *reinterpret_cast<u32x4_t *>(kr + 48) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c1[0], d2, v);
+    *reinterpret_cast<u32x4_t *>(kr + 64) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c1[1], d2, v);
+    *reinterpret_cast<u32x4_t *>(kr + 80) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c1[2], d3, v);
+    *reinterpret_cast<u32x4_t *>(kr + 96) = u32x4_t{v[0], v[1], v[2], v[3]};
+    e2m1x8_to_half_cvt(R.c1[3], d3, v);
+    *reinterpret_cast<u32x4_t *>(kr + 112) = u32x4_t{v[0], v[1], v[2], v[3]};
+    uint32_t h[4];
+    e4m3x4_to_half_cvt(rp[0], h);
+    e4m3x4_to_half_cvt(rp[1], h + 2);
+    *reinterpret_cast<u32x4_t *>(ktile + krow(gr) + 16 * (64 + gp)) = u32x4_t{h[0], h[1], h[2], h[3]};
+}
+
+constexpr int kPosPerLane = kSlotCap / 256;
 
 template <bool QF32>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
-    __shared__ uint32_t lds[kLdsDw];
-    uint32_t *ktile = lds;
-    uint32_t *vt = lds + kKTileDw;
-    int32_t *slots = reinterpret_cast<int32_t *>(lds + kKTileDw + kVtDw);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    floatx4_t *xbuf = reinterpret_cast<floatx4_t *>(lds + 2 * kKTileBytes);
+    int32_t *redo = reinterpret_cast<int32_t *>(lds + 2 * kKTileBytes + kXBytes - 16);
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + 2 * kKTileBytes + kXBytes);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x, split = blockIdx.y;
-    const int hg = blockIdx.z * 4 + wave;
-    const bool active = hg < (p.n_heads >> 4);
-    const int lr = lane & 15, g = lane >> 4;
-    const int head = hg * 16 + lr;
+    const int hg = blockIdx.z * 2 + (wave >> 1);
+    const int half = wave & 1;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int head = hg * 32 + l32;
+    const bool group_live = hg * 32 < p.n_heads;
+    const bool head_live = head < p.n_heads;
 
     const int n_tiles = (p.k + kTile - 1) / kTile;
     const int t_lo = split * p.tiles_per_split;
@@ -71,35 +145,89 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     const int e_lo = t_lo * kTile;
     const int e_hi = min(p.k, t_hi * kTile);
 
-    // ---- queries: B operand of S^T = K Q^T.  Lane (lr, g) holds head lr,
-    // dims 32ks + 8g .. +7 for ks = 0..17.
+    const int32_t req = p.row_req ? p.row_req[r] : r;
+    const bool bad_req = p.page_table && (req < 0 || req >= p.pt_n_rows);
+    const int32_t *pt_row = p.page_table && !bad_req ? p.page_table + (int64_t)req * p.pt_row_stride : nullptr;
+    const int32_t *list = p.topk + (int64_t)r * p.topk_row_stride;
+    uint32_t err = 0;
+
+    // Translation of a chunk of at most kSlotCap entries into slots[]: the
+    // list entries first, then their page-table entries, each batch issued
+    // before any of it is used.
+    int32_t pos[kPosPerLane], phys[kPosPerLane];
+    auto load_positions = [&](int c_lo, int c_hi) {
+#pragma unroll
+        for (int i = 0; i < kPosPerLane; ++i) {
+            const int e = tid + 256 * i;
+            pos[i] = c_lo + e < c_hi ? list[c_lo + e] : -1;
+        }
+    };
+    auto load_pages = [&]() {
+#pragma unroll
+        for (int i = 0; i < kPosPerLane; ++i) {
+            phys[i] = -1;
+            if (pt_row && pos[i] >= 0 && (pos[i] >> p.page_shift) < p.pt_n_pages) phys[i] = pt_row[pos[i] >> p.page_shift];
+        }
+    };
+    auto write_slots = [&](int n_entries) {
+#pragma unroll
+        for (int i = 0; i < kPosPerLane; ++i) {
+            const int e = tid + 256 * i;
+            if (e >= n_entries) break;
+            int64_t s = -1;
+            if (bad_req) err |= pos[i] >= 0 ? kErrPage : 0u;
+            else s = slot_of(pos[i], phys[i], pt_row != nullptr, p.pt_n_pages, p.page_shift, p.n_slots, err);
+            slots[e] = (int32_t)s;
+        }
+    };
+
+    // first chunk's list entries are in flight while the queries load
+    const int first_hi = min(e_hi, e_lo + kSlotCap);
+    if (e_lo < e_hi) load_positions(e_lo, first_hi);
+
+    // ---- queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head l32,
+    // dims 288*half + 16ks + 8g .. +7 for ks = 0..17.  The power-of-two scale
+    // qs puts the head's largest |q| in [2^13, 2^14): exact in fp16.  All of
+    // the head's loads are issued before any is used.
     half8_t qb[18];
     half8_t ql[QF32 ? 18 : 1];
     float score_mul = 0.0f;
-    if (active) {
-        const int64_t qoff = (int64_t)r * p.q_row_stride + (int64_t)head * p.q_head_stride + 8 * g;
+    {
+        const int64_t hoff = (int64_t)r * p.q_row_stride + (int64_t)head * p.q_head_stride + 8 * g;
         float qmax = 0.0f;
         if constexpr (QF32) {
-            const float *qp = reinterpret_cast<const float *>(p.q) + qoff;
-            float4 raw[36];
+            const float *qp = reinterpret_cast<const float *>(p.q) + hoff;
+            float4 own[36];
+            float4 other[36];
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                raw[2 * ks] = *reinterpret_cast<const float4 *>(qp + 32 * ks);
-                raw[2 * ks + 1] = *reinterpret_cast<const float4 *>(qp + 32 * ks + 4);
+                const int mine = 288 * half + 16 * ks, theirs = 288 * (half ^ 1) + 16 * ks;
+                own[2 * ks] = own[2 * ks + 1] = other[2 * ks] = other[2 * ks + 1] = float4{0, 0, 0, 0};
+                if (head_live) {
+                    own[2 * ks] = *reinterpret_cast<const float4 *>(qp + mine);
+                    own[2 * ks + 1] = *reinterpret_cast<const float4 *>(qp + mine + 4);
+                    other[2 * ks] = *reinterpret_cast<const float4 *>(qp + theirs);
+                    other[2 * ks + 1] = *reinterpret_cast<const float4 *>(qp + theirs + 4);
+                }
             }
+            if (e_lo < e_hi) load_pages();
 #pragma unroll
-            for (int i = 0; i < 36; ++i)
-                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(raw[i].x), __builtin_fabsf(raw[i].y)),
-                                                             __builtin_fmaxf(__builtin_fabsf(raw[i].z), __builtin_fabsf(raw[i].w))));
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 16));
+            for (int i = 0; i < 36; ++i) {
+                const float4 a = own[i], b = other[i];
+                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)),
+                                                             __builtin_fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))));
+                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)),
+                                                             __builtin_fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
+            }
             qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
             int ex = 0;
             if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
+            score_mul = p.score_mul / qs;
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                const float v[8] = {raw[2 * ks].x, raw[2 * ks].y, raw[2 * ks].z, raw[2 * ks].w,
-                                    raw[2 * ks + 1].x, raw[2 * ks + 1].y, raw[2 * ks + 1].z, raw[2 * ks + 1].w};
+                const float v[8] = {own[2 * ks].x, own[2 * ks].y, own[2 * ks].z, own[2 * ks].w,
+                                    own[2 * ks + 1].x, own[2 * ks + 1].y, own[2 * ks + 1].z, own[2 * ks + 1].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = v[e] * qs;
@@ -108,211 +236,193 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
                     ql[ks][e] = (_Float16)(x - (float)hi);
                 }
             }
-            score_mul = p.score_mul / qs;
         } else {
-            const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) + qoff;
-            u32x4_t raw[18];
+            const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) + hoff;
+            u32x4_t own[18], other[18];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) raw[ks] = *reinterpret_cast<const u32x4_t *>(qp + 32 * ks);
+            for (int ks = 0; ks < 18; ++ks) {
+                own[ks] = other[ks] = u32x4_t{0, 0, 0, 0};
+                if (head_live) {
+                    own[ks] = *reinterpret_cast<const u32x4_t *>(qp + 288 * half + 16 * ks);
+                    other[ks] = *reinterpret_cast<const u32x4_t *>(qp + 288 * (half ^ 1) + 16 * ks);
+                }
+            }
+            if (e_lo < e_hi) load_pages();
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint32_t w = raw[ks][c];
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w << 16)),
-                                                                 __builtin_fabsf(__uint_as_float(w & 0xFFFF0000u))));
+                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(own[ks][c] << 16)),
+                                                                 __builtin_fabsf(__uint_as_float(own[ks][c] & 0xFFFF0000u))));
+                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(other[ks][c] << 16)),
+                                                                 __builtin_fabsf(__uint_as_float(other[ks][c] & 0xFFFF0000u))));
                 }
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 16));
             qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
             int ex = 0;
             if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
-            const float qs = __builtin_ldexpf(1.0f, 14 - ex);
+            const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
+            score_mul = p.score_mul / qs;
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint32_t w = raw[ks][c];
-                    qb[ks][2 * c] = (_Float16)(__uint_as_float(w << 16) * qs);
-                    qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(w & 0xFFFF0000u) * qs);
+                    qb[ks][2 * c] = (_Float16)(__uint_as_float(own[ks][c] << 16) * qs);
+                    qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(own[ks][c] & 0xFFFF0000u) * qs);
                 }
-            score_mul = p.score_mul / qs;
         }
     }
+    // pad to whole tiles: entries past the chunk's end get slot -1
+    if (e_lo < e_hi) write_slots((first_hi - e_lo + kTile - 1) / kTile * kTile);
+    if (tid == 0) *redo = 0;                       // set only in pass 0; read after its last barrier
+    __syncthreads();
 
-    floatx4_t o[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -__builtin_inff();
+    floatx16_t o[8];
+    float m_ref = -__builtin_inff();   // reference of P = 2^(s - m_ref) for this lane's head
+    float m_max = -__builtin_inff();   // largest score seen (the exact maximum after a pass)
     float l_run = 0.0f;
-    uint32_t err = 0;
 
-    const int32_t req = p.row_req ? p.row_req[r] : r;
-    const bool bad_req = p.page_table && (req < 0 || req >= p.pt_n_rows);
-    const int32_t *pt_row = p.page_table && !bad_req ? p.page_table + (int64_t)req * p.pt_row_stride : nullptr;
-    const int32_t *list = p.topk + (int64_t)r * p.topk_row_stride;
+    const int gr = tid & 31, gp = tid >> 5;        // gather role: row gr, part gp
+    // score operand: row l32, chunk 36*half + 2ks + g
+    const int qk_off = krow(l32) + 16 * (36 * half + g);
+    // transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
+    // second read of a k-half, +16 for the second k-half), 8 bytes at latent
+    // dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
+    const int tr_off = krow(4 * g + ((lane >> 2) & 3)) + 2 * (256 * half + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-    // gather lane roles
-    const int pp = tid & 15;          // rows 2pp, 2pp+1 of the tile
-    const int qc = tid >> 4;          // 16-byte code chunk: latent dims 32qc..32qc+31
-    const int rope_row = tid >> 2;    // tid < 128: rope bytes 16*(tid&3).. of row tid>>2
-    const int vt_dw_pair = vt_pair_dw(pp);
-
-    u32x4_t ca, cb, rp;
-    uint32_t sab;
-
-    auto gather = [&](int tile) {
-        const int32_t sa = slots[tile * kTile + 2 * pp];
-        const int32_t sb = slots[tile * kTile + 2 * pp + 1];
-        ca = u32x4_t{0, 0, 0, 0};
-        cb = u32x4_t{0, 0, 0, 0};
-        rp = u32x4_t{0, 0, 0, 0};
-        uint32_t s0 = 0, s1 = 0;
-        if (sa >= 0) {
-            const uint8_t *row = p.pool + (int64_t)sa * kRowBytes;
-            ca = *reinterpret_cast<const u32x4_t *>(row + 16 * qc);
-            s0 = *reinterpret_cast<const uint16_t *>(row + kScaleOff + 2 * qc);
-        }
-        if (sb >= 0) {
-            const uint8_t *row = p.pool + (int64_t)sb * kRowBytes;
-            cb = *reinterpret_cast<const u32x4_t *>(row + 16 * qc);
-            s1 = *reinterpret_cast<const uint16_t *>(row + kScaleOff + 2 * qc);
-        }
-        sab = s0 | (s1 << 16);
-        if (tid < 128) {
-            const int32_t sr = slots[tile * kTile + rope_row];
-            if (sr >= 0)
-                rp = *reinterpret_cast<const u32x4_t *>(p.pool + (int64_t)sr * kRowBytes + kRopeOff + 16 * (tid & 3));
-        }
-    };
-
-    auto dequant_store = [&]() {
-        const half2_t da0 = block_scale_half(sab & 0xFFu), da1 = block_scale_half((sab >> 8) & 0xFFu);
-        const half2_t db0 = block_scale_half((sab >> 16) & 0xFFu), db1 = block_scale_half(sab >> 24);
-        uint32_t *ka_row = ktile + (2 * pp) * kKPitchDw + 16 * qc;
-        uint32_t *kb_row = ka_row + kKPitchDw;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            uint32_t ka[4], kb[4];
-            e2m1x8_to_half(ca[c], c < 2 ? da0 : da1, ka);
-            e2m1x8_to_half(cb[c], c < 2 ? db0 : db1, kb);
-            *reinterpret_cast<u32x4_t *>(ka_row + 4 * c) = u32x4_t{ka[0], ka[1], ka[2], ka[3]};
-            *reinterpret_cast<u32x4_t *>(kb_row + 4 * c) = u32x4_t{kb[0], kb[1], kb[2], kb[3]};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * qc + 8 * c + 2 * i;
-                vt[vt_addr(d0, vt_dw_pair)] = __builtin_amdgcn_perm(kb[i], ka[i], 0x05040100u);
-                vt[vt_addr(d0 + 1, vt_dw_pair)] = __builtin_amdgcn_perm(kb[i], ka[i], 0x07060302u);
-            }
-        }
-        if (tid < 128) {
-            uint32_t h[8];
-            dequant_rope16(rp, h);
-            uint32_t *dst = ktile + rope_row * kKPitchDw + kLatent / 2 + 8 * (tid & 3);
-            *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{h[0], h[1], h[2], h[3]};
-            *reinterpret_cast<u32x4_t *>(dst + 4) = u32x4_t{h[4], h[5], h[6], h[7]};
-        }
-    };
-
-    const _Float16 *kth = reinterpret_cast<const _Float16 *>(ktile);
-
-    for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
-        const int c_hi = min(e_hi, c_lo + kSlotCap);
-        const int n_t = (c_hi - c_lo + kTile - 1) / kTile;
-        __syncthreads();                               // slots of the previous chunk are no longer read
-        for (int e = tid; e < n_t * kTile; e += 256) {
-            int64_t s = -1;
-            if (c_lo + e < c_hi) {
-                const int32_t pos = list[c_lo + e];
-                if (bad_req) err |= pos >= 0 ? kErrPage : 0u;
-                else s = translate_slot(pos, pt_row, p.pt_n_pages, p.page_shift, p.n_slots, err);
-            }
-            slots[e] = (int32_t)s;
-        }
-        __syncthreads();
-        gather(0);
-        for (int tt = 0; tt < n_t; ++tt) {
-            dequant_store();
-            const bool valid_lane = lane < kTile && slots[tt * kTile + lane] >= 0;
-            const uint64_t vmask = __ballot(valid_lane);
-            __syncthreads();
-            if (tt + 1 < n_t) gather(tt + 1);
-            if (active) {
-                // ---- scores S^T[32 rows x 16 heads]
-                floatx4_t s0a = {0, 0, 0, 0}, s0b = {0, 0, 0, 0}, s1a = {0, 0, 0, 0}, s1b = {0, 0, 0, 0};
+    // One tile: scores from buffer tt&1 while rows of tile tt+1 (held in nxt)
+    // are dequantized into the other buffer and rows of tile tt+3 are
+    // requested into nxt; then softmax and P.V.
+    auto tile_step = [&](int tt, int n_t, RowPart &nxt) {
+        const uint8_t *kcur = lds + (tt & 1) * kKTileBytes;
+        const uint64_t vmask = __ballot(lane < kTile && slots[tt * kTile + lane] >= 0);
+        floatx16_t sacc = {};
+        if (group_live) {
+            if constexpr (QF32) {
 #pragma unroll
                 for (int ks = 0; ks < 18; ++ks) {
-                    const half8_t a0 = *reinterpret_cast<const half8_t *>(kth + lr * kKPitchHalf + 32 * ks + 8 * g);
-                    const half8_t a1 = *reinterpret_cast<const half8_t *>(kth + (16 + lr) * kKPitchHalf + 32 * ks + 8 * g);
-                    if (ks & 1) {
-                        s0b = mfma16(a0, qb[ks], s0b);
-                        s1b = mfma16(a1, qb[ks], s1b);
-                        if constexpr (QF32) {
-                            s0a = mfma16(a0, ql[ks], s0a);
-                            s1a = mfma16(a1, ql[ks], s1a);
-                        }
-                    } else {
-                        s0a = mfma16(a0, qb[ks], s0a);
-                        s1a = mfma16(a1, qb[ks], s1a);
-                        if constexpr (QF32) {
-                            s0b = mfma16(a0, ql[ks], s0b);
-                            s1b = mfma16(a1, ql[ks], s1b);
-                        }
-                    }
+                    const half8_t a = *reinterpret_cast<const half8_t *>(kcur + qk_off + 32 * ks);
+                    sacc = mfma32(a, qb[ks], sacc);
+                    sacc = mfma32(a, ql[ks], sacc);
+                    if (ks % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bound the read-ahead window
                 }
-                const floatx4_t s0 = s0a + s0b, s1 = s1a + s1b;
-                // ---- online softmax (base 2).  Lane holds rows 4g+i and 16+4g+i of head lr.
-                float sc[8];
+            } else {
+                floatx16_t s2 = {};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ra = 4 * g + i, rb = 16 + 4 * g + i;
-                    sc[i] = ((vmask >> ra) & 1) ? s0[i] * score_mul : -__builtin_inff();
-                    sc[4 + i] = ((vmask >> rb) & 1) ? s1[i] * score_mul : -__builtin_inff();
+                for (int ks = 0; ks < 18; ++ks) {
+                    const half8_t a = *reinterpret_cast<const half8_t *>(kcur + qk_off + 32 * ks);
+                    if (ks & 1) s2 = mfma32(a, qb[ks], s2);
+                    else sacc = mfma32(a, qb[ks], sacc);
                 }
-                float tmax = sc[0];
+                sacc += s2;
+            }
+        }
+        if (tt + 1 < n_t) dequant_part(lds + ((tt + 1) & 1) * kKTileBytes, gr, gp, nxt);
+        if (tt + 3 < n_t) gather_part(p.pool, slots[(tt + 3) * kTile + gr], gp, nxt);
+        if (group_live) {
 #pragma unroll
-                for (int i = 1; i < 8; ++i) tmax = __builtin_fmaxf(tmax, sc[i]);
-                tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
-                tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-                const bool need = tmax > m_run + kRescaleSlack;
-                if (__any(need)) {
-                    const float m_new = need ? tmax : m_run;
-                    const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-                    l_run *= alpha;
+            for (int q4 = 0; q4 < 4; ++q4)
+                xbuf[(wave * 4 + q4) * 64 + lane] = floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+        }
+        __syncthreads();                           // partial scores and the next tile visible
+        if (group_live) {
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) o[i] *= alpha;
-                    m_run = m_new;
-                }
-                half8_t pb;
-                float lsum = 0.0f;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const floatx4_t o4 = xbuf[((wave ^ 1) * 4 + q4) * 64 + lane];
+                sacc[4 * q4] += o4[0];
+                sacc[4 * q4 + 1] += o4[1];
+                sacc[4 * q4 + 2] += o4[2];
+                sacc[4 * q4 + 3] += o4[3];
+            }
+            // ---- softmax numerators.  Register v holds row 8(v/4) + 4g + v%4.
+            float sc16[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pv = sc[i] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m_run);
-                    lsum += pv;
-                    pb[i] = (_Float16)pv;
-                }
-                l_run += lsum;
-                // ---- O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16]
+            for (int v = 0; v < 16; ++v) sc16[v] = sacc[v] * score_mul;
+            if ((uint32_t)vmask != 0xFFFFFFFFu) {      // a tile with skipped entries
 #pragma unroll
-                for (int md = 0; md < 32; ++md) {
-                    const int d = 16 * md + lr;
-                    const half8_t a = *reinterpret_cast<const half8_t *>(vt + vt_addr(d, 4 * g));
-                    o[md] = mfma16(a, pb, o[md]);
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 8 * (v >> 2) + 4 * g + (v & 3);
+                    if (!((vmask >> row) & 1)) sc16[v] = -__builtin_inff();
                 }
             }
-            __syncthreads();
+            float tmax = sc16[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) tmax = __builtin_fmaxf(tmax, sc16[v]);
+            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+            m_max = __builtin_fmaxf(m_max, tmax);
+            if (m_ref == -__builtin_inff()) m_ref = tmax;    // first tile with a valid entry
+            if (tmax > m_ref + kRefSlack) *redo = 1;         // P could overflow fp16 (pass 0 only)
+            half8_t pb0, pb1;
+            float lsum = 0.0f;
+            const float mr = m_ref == -__builtin_inff() ? 0.0f : m_ref;   // nothing valid so far
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float pv = __builtin_amdgcn_exp2f(sc16[v] - mr);   // exp2(-inf) = 0
+                lsum += pv;
+                if (v < 8) pb0[v] = (_Float16)pv;
+                else pb1[v - 8] = (_Float16)pv;
+            }
+            l_run += lsum;
+            // ---- O^T[256 x 32] += V^T P^T, V^T through transposing reads
+#pragma unroll
+            for (int md = 0; md < 8; ++md) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const short4_t lo = lds_read_tr16(kcur, tr_off + kKRowBytes * (16 * kk) + 64 * md);
+                    const short4_t hi = lds_read_tr16(kcur, tr_off + kKRowBytes * (16 * kk + 8) + 64 * md);
+                    const half8_t a = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
+                }
+                if constexpr (QF32) __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        __syncthreads();                           // this tile's buffer and the partial scores are free
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = floatx16_t{};
+        l_run = 0.0f;
+        if (pass == 1) m_ref = m_max;              // the exact maximum: no P can exceed 1
+        for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
+            const int c_hi = min(e_hi, c_lo + kSlotCap);
+            const int n_t = (c_hi - c_lo + kTile - 1) / kTile;
+            if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) {
+                __syncthreads();                   // slots of the previous chunk are no longer read
+                load_positions(c_lo, c_hi);
+                load_pages();
+                write_slots(n_t * kTile);
+                __syncthreads();
+            }
+            RowPart ra, rb;
+            gather_part(p.pool, slots[gr], gp, ra);
+            if (n_t > 1) gather_part(p.pool, slots[kTile + gr], gp, rb);
+            dequant_part(lds, gr, gp, ra);
+            if (n_t > 2) gather_part(p.pool, slots[2 * kTile + gr], gp, ra);
+            __syncthreads();                       // tile 0 in buffer 0
+            for (int tt = 0; tt < n_t; tt += 2) {
+                tile_step(tt, n_t, rb);            // rb: tile tt+1 -> buffer, then tile tt+3
+                if (tt + 1 < n_t) tile_step(tt + 1, n_t, ra);   // ra: tile tt+2 -> buffer, then tile tt+4
+            }
+        }
+        if (pass == 1 || *redo == 0) break;        // uniform: read after the last barrier
     }
 
     if (err && p.err_word) atomicOr(p.err_word, err);
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (!active) return;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float m_fin = m_ref == -__builtin_inff() ? 0.0f : m_ref;
+    if (!head_live) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     float *orow = p.out + (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)head * kLatent;
 #pragma unroll
-    for (int md = 0; md < 32; ++md) *reinterpret_cast<floatx4_t *>(orow + 16 * md + 4 * g) = o[md] * inv;
-    if (g == 0 && p.lse) {
-        const float lse = l_tot > 0.0f ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
+    for (int md = 0; md < 8; ++md)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = 256 * half + 32 * md + 8 * j + 4 * g;
+            *reinterpret_cast<floatx4_t *>(orow + d) =
+                floatx4_t{o[md][4 * j], o[md][4 * j + 1], o[md][4 * j + 2], o[md][4 * j + 3]} * inv;
+        }
+    if (half == 0 && g == 0 && p.lse) {
+        const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
         p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
     }
 }

@@ -110,6 +110,23 @@ __device__ __forceinline__ void e2m1x8_to_half(uint32_t w, half2_t d, uint32_t o
     out[3] = __builtin_bit_cast(uint32_t, h3);
 }
 
+// Same result as e2m1x8_to_half with gfx950's FP4 -> fp16 conversion at
+// scale 1 (exact; the code byte's low nibble is the first element) followed by
+// one packed multiply by the block scale.
+__device__ __forceinline__ void e2m1x8_to_half_cvt(uint32_t w, half2_t d, uint32_t out[4]) {
+    out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * d);
+    out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * d);
+    out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * d);
+    out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * d);
+}
+
+// Four E4M3 codes -> two fp16 pairs with gfx950's FP8 (OCP E4M3) -> fp16
+// conversion at scale 1, exact for every code.
+__device__ __forceinline__ void e4m3x4_to_half_cvt(uint32_t w, uint32_t out[2]) {
+    out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
 // Two E4M3 codes (bytes lo, hi of a 16-bit field) -> fp16 pair, exact.
 // Magnitude bits placed at fp16 bits 13..7 read as 2^-8 times the E4M3 value
 // (subnormal codes become fp16 subnormals), so one multiply by 256 finishes.
@@ -146,6 +163,22 @@ __device__ __forceinline__ void dequant_rope16(u32x4_t bytes, uint32_t out[8]) {
 }
 
 // ----------------------------------------------------------------- misc
+
+// The same translation with the page-table entry already loaded (phys is
+// pt_row[pos >> page_shift] when that page is inside the table).
+__device__ __forceinline__ int64_t slot_of(int32_t pos, int32_t phys, bool paged, int32_t pt_n_pages,
+                                           int32_t page_shift, int64_t n_slots, uint32_t &err) {
+    if (pos < 0) return -1;
+    int64_t slot;
+    if (paged) {
+        if ((pos >> page_shift) >= pt_n_pages || phys < 0) { err |= kErrPage; return -1; }
+        slot = ((int64_t)phys << page_shift) + (pos & ((1 << page_shift) - 1));
+    } else {
+        slot = pos;
+    }
+    if (slot >= n_slots) { err |= kErrSlot; return -1; }
+    return slot;
+}
 
 __device__ __forceinline__ int64_t translate_slot(int32_t pos, const int32_t *pt_row, int32_t pt_n_pages,
                                                   int32_t page_shift, int64_t n_slots, uint32_t &err) {

@@ -268,3 +268,18 @@ def test_graph_replay_matches_eager_bitwise():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), "replay %d differs" % i
+
+
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_rising_scores_take_the_exact_second_pass(num_splits):
+    """Lists ordered by increasing score with large queries: the first tile's
+    maximum sits far below later scores (P would overflow fp16 against it), so
+    the kernel must fall back to its second pass with the exact maximum."""
+    spec = W.scaled(SMALL, k=512, ctx=2048)
+    pool_d, pool_h = pools(spec)
+    q = (W.queries(spec).float() * 40.0).to(torch.bfloat16)
+    topk, pt = W.topk_lists(spec), W.page_table(spec)
+    _, _, _, probs = oracle.sparse_mla(q_for_oracle(q), pool_h, topk, spec.sm_scale, page_table=pt, want_probs=True)
+    order = np.argsort(np.log(probs[:, 0, :] + 1e-300), axis=1)          # head 0's scores, ascending
+    rising = np.take_along_axis(topk, order, axis=1).astype(np.int32)
+    _run(spec, q, rising, pt, num_splits=num_splits)
