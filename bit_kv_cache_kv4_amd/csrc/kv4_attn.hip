@@ -39,37 +39,59 @@
 #include "kv4_device.h"
 #include "kv4_launch.h"
 
+#include <type_traits>
+
 namespace kv4 {
 
 constexpr int kTile = 32;                              // list entries per tile
-constexpr int kKChunks = 80;                           // 16-byte chunks per K-tile row (72 used)
-constexpr int kKRowBytes = kKChunks * 16;
-constexpr int kKTileBytes = kTile * kKRowBytes;        // 40960
-constexpr int kXBytes = 4 * 64 * 16 * 4 + 16;          // partial scores: 4 wavefronts x 64 lanes x 16, + a flag
-constexpr int kSlotCap = 2048;                         // entries translated per chunk
-constexpr int kLdsBytes = 2 * kKTileBytes + kXBytes + kSlotCap * 4;   // 106496
+constexpr int kKChunks = 76;                           // 16-byte chunks per K-tile row: 72 + shift
+constexpr int kKRowBytes = kKChunks * 16;              // 1216
+constexpr int kKTileBytes = kTile * kKRowBytes;        // 38912
+constexpr int kXBytes = 4 * 64 * 16 * 4;               // partial scores: 4 wavefronts x 64 lanes x 16
+constexpr int kSlotCap = 1024;                         // entries translated per chunk
+constexpr int kKBufs = 3;                              // K tiles in flight: P.V(t), scores(t+1), dequant(t+2)
+constexpr int kSlotOff = kKBufs * kKTileBytes + 2 * kXBytes + 16;
+constexpr int kCountOff = kSlotOff + kSlotCap * 4;   // valid entries per (batch, wavefront) of a chunk
+constexpr int kLdsBytes = kCountOff + 64;             // 153680
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// K-tile layout: row r starts at r * 1280 + 16 * krot(r) bytes (chunks of 16
-// bytes, 72 used, up to 7 chunks of shift).  krot maps eight consecutive rows
-// onto eight distinct 16-byte bank groups, so the score operand reads (one
-// chunk of rows r..r+7) are conflict-free, and rows 4g..4g+3 start 32 bytes
-// apart modulo 128, so the transposing reads (32 bytes of each of 4 rows) are
-// too.  Every address is a per-lane base plus a compile-time offset.
-__device__ __forceinline__ int krot(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
-__device__ __forceinline__ int krow(int r) { return r * kKRowBytes + 16 * krot(r); }
+// K-tile layout for gfx950's LDS (64 banks of 4 bytes, 256 bytes a clock):
+// row r starts at r * 1216 + 16 * ((r >> 2) & 3).  In 16-byte slots modulo
+// 256 bytes that is 12r + (r >> 2) mod 16, so rows 0..15 (and 16..31) sit in
+// 16 distinct slots: the score reads and the dequantizing writes (16 rows per
+// 16 lanes) are conflict-free.  Rows 4m..4m+3 sit in slots congruent modulo
+// 4, so their 64-byte spans in a transposing read (4 rows x 64 bytes per 32
+// lanes) tile the 256 bytes.  Every address is a per-lane base plus a
+// compile-time offset.
+__host__ __device__ constexpr int krow(int r) { return r * kKRowBytes + 16 * ((r >> 2) & 3); }
+static_assert(krow(kTile - 1) + 2 * kDim <= kKTileBytes, "K-tile rows overlap");
 
 __device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ short4_t lds_read_tr16(const uint8_t *lds_base, int byte_off) {
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_short4 *)((__attribute__((address_space(3))) uint8_t *)lds_base + byte_off));
+// LDS accesses by 32-bit byte address.  Each step pins (makes opaque to the
+// optimiser) one per-lane base per access pattern, so every access of the step
+// is that base plus a constant the instruction's offset field holds.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+__device__ __forceinline__ uint32_t lds_addr(uint8_t *p) { return (uint32_t)(size_t)(lds_u8_t *)p; }
+__device__ __forceinline__ uint32_t pin(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t a) {
+    return *(const __attribute__((address_space(3))) T *)(size_t)a;
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(uint32_t a, T v) {
+    *(__attribute__((address_space(3))) T *)(size_t)a = v;
+}
+__device__ __forceinline__ short4_t lds_read_tr16(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t *)(size_t)a);
 }
 
 // One lane's share of a tile's rows: row t % 32, part t / 32 (latent dims
@@ -81,44 +103,36 @@ struct RowPart {
     bool valid;
 };
 
-// A skipped entry reads row 0 (the pool has at least one row whenever a slot
-// can be valid) and is zeroed by dequant_part: scale and rope bytes become 0.
-__device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, int32_t slot, int gp, RowPart &R) {
+// A skipped entry reads 352 readable bytes elsewhere (`stand_in`: the query
+// row, at least 1152 bytes, so an empty pool is never touched) and is zeroed by
+// dequant_part: scale and rope bytes become 0, so every value is 0.
+__device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, const uint8_t *stand_in, int32_t slot,
+                                            int gp, RowPart &R) {
     R.valid = slot >= 0;
-    const uint8_t *row = pool + (int64_t)(R.valid ? slot : 0) * kRowBytes;
+    const uint8_t *row = R.valid ? pool + (int64_t)slot * kRowBytes : stand_in;
     R.c0 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp);
     R.c1 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp + 16);
     R.sc = *reinterpret_cast<const uint32_t *>(row + kScaleOff + 4 * gp);
     R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
 }
 
-__device__ __forceinline__ void dequant_part(uint8_t *ktile, int gr, int gp, const RowPart &R) {
+// dq = K-tile row base + 128 * part (latent chunks), rq = row base + 16 * (64 + part)
+__device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const RowPart &R) {
     const uint32_t sc = R.valid ? R.sc : 0u;
     const u32x2_t rp = R.valid ? R.rp : u32x2_t{0, 0};
-    const half2_t d0 = block_scale_half(sc & 0xFFu), d1 = block_scale_half((sc >> 8) & 0xFFu);
-    const half2_t d2 = block_scale_half((sc >> 16) & 0xFFu), d3 = block_scale_half(sc >> 24);
-    uint8_t *kr = ktile + krow(gr) + 128 * gp;
-    uint32_t v[4];
-    e2m1x8_to_half_cvt(R.c0[0], d0, v);
-    *reinterpret_cast<u32x4_t *>(kr + 0) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c0[1], d0, v);
-    *reinterpret_cast<u32x4_t *>(kr + 16) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c0[2], d1, v);
-    *reinterpret_cast<u32x4_t *>(kr + 32) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c0[3], d1, v);
-    *reinterpret_cast<u32x4_t *>(kr + 48) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c1[0], d2, v);
-    *reinterpret_cast<u32x4_t *>(kr + 64) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c1[1], d2, v);
-    *reinterpret_cast<u32x4_t *>(kr + 80) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c1[2], d3, v);
-    *reinterpret_cast<u32x4_t *>(kr + 96) = u32x4_t{v[0], v[1], v[2], v[3]};
-    e2m1x8_to_half_cvt(R.c1[3], d3, v);
-    *reinterpret_cast<u32x4_t *>(kr + 112) = u32x4_t{v[0], v[1], v[2], v[3]};
+    half2_t d[4];
+    block_scales_half_cvt(sc, d);
+    const uint32_t c[8] = {R.c0[0], R.c0[1], R.c0[2], R.c0[3], R.c1[0], R.c1[1], R.c1[2], R.c1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t v[4];
+        e2m1x8_to_half_cvt(c[i], d[i >> 1], v);
+        lds_st<u32x4_t>(dq + 16 * i, u32x4_t{v[0], v[1], v[2], v[3]});
+    }
     uint32_t h[4];
     e4m3x4_to_half_cvt(rp[0], h);
     e4m3x4_to_half_cvt(rp[1], h + 2);
-    *reinterpret_cast<u32x4_t *>(ktile + krow(gr) + 16 * (64 + gp)) = u32x4_t{h[0], h[1], h[2], h[3]};
+    lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
 }
 
 constexpr int kPosPerLane = kSlotCap / 256;
@@ -126,9 +140,9 @@ constexpr int kPosPerLane = kSlotCap / 256;
 template <bool QF32>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    floatx4_t *xbuf = reinterpret_cast<floatx4_t *>(lds + 2 * kKTileBytes);
-    int32_t *redo = reinterpret_cast<int32_t *>(lds + 2 * kKTileBytes + kXBytes - 16);
-    int32_t *slots = reinterpret_cast<int32_t *>(lds + 2 * kKTileBytes + kXBytes);
+    int32_t *redo = reinterpret_cast<int32_t *>(lds + kKBufs * kKTileBytes + 2 * kXBytes);
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + kSlotOff);
+    int32_t *counts = reinterpret_cast<int32_t *>(lds + kCountOff);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x, split = blockIdx.y;
@@ -151,9 +165,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     const int32_t *list = p.topk + (int64_t)r * p.topk_row_stride;
     uint32_t err = 0;
 
-    // Translation of a chunk of at most kSlotCap entries into slots[]: the
-    // list entries first, then their page-table entries, each batch issued
-    // before any of it is used.
+    // Translation of a chunk of at most kSlotCap entries: the list entries
+    // first, then their page-table entries, each batch issued before any of it
+    // is used.  write_slots packs the valid entries' slots, in list order, to
+    // the front of slots[] and pads the last tile with -1, so every tile but
+    // the last is full; it returns the number of valid entries (the same in
+    // every thread) and holds a barrier, so all threads call it.
     int32_t pos[kPosPerLane], phys[kPosPerLane];
     auto load_positions = [&](int c_lo, int c_hi) {
 #pragma unroll
@@ -169,21 +186,43 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             if (pt_row && pos[i] >= 0 && (pos[i] >> p.page_shift) < p.pt_n_pages) phys[i] = pt_row[pos[i] >> p.page_shift];
         }
     };
-    auto write_slots = [&](int n_entries) {
+    auto write_slots = [&]() -> int {
+        int32_t sl[kPosPerLane];
+        uint64_t bal[kPosPerLane];
 #pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {
-            const int e = tid + 256 * i;
-            if (e >= n_entries) break;
+        for (int i = 0; i < kPosPerLane; ++i) {       // entry e = tid + 256 i: list order is (i, wave, lane)
             int64_t s = -1;
             if (bad_req) err |= pos[i] >= 0 ? kErrPage : 0u;
             else s = slot_of(pos[i], phys[i], pt_row != nullptr, p.pt_n_pages, p.page_shift, p.n_slots, err);
-            slots[e] = (int32_t)s;
+            sl[i] = (int32_t)s;
+            bal[i] = __ballot(s >= 0);
+            if (lane == 0) counts[4 * i + wave] = (int32_t)__popcll(bal[i]);
         }
+        __syncthreads();
+        int nv = 0, base[kPosPerLane];
+#pragma unroll
+        for (int i = 0; i < kPosPerLane; ++i) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if (w == wave) base[i] = nv;
+                nv += counts[4 * i + w];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPosPerLane; ++i) {
+            const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u));
+            if (sl[i] >= 0) slots[base[i] + below] = sl[i];
+            const int e = tid + 256 * i;
+            if (e >= nv && e < ((nv + kTile - 1) & ~(kTile - 1))) slots[e] = -1;
+        }
+        return nv;
     };
 
     // first chunk's list entries are in flight while the queries load
     const int first_hi = min(e_hi, e_lo + kSlotCap);
     if (e_lo < e_hi) load_positions(e_lo, first_hi);
+    else load_positions(0, 0);
 
     // ---- queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head l32,
     // dims 288*half + 16ks + 8g .. +7 for ks = 0..17.  The power-of-two scale
@@ -271,8 +310,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
                 }
         }
     }
-    // pad to whole tiles: entries past the chunk's end get slot -1
-    if (e_lo < e_hi) write_slots((first_hi - e_lo + kTile - 1) / kTile * kTile);
+    int nv = e_lo < e_hi ? write_slots() : 0;      // valid entries of the current chunk
     if (tid == 0) *redo = 0;                       // set only in pass 0; read after its last barrier
     __syncthreads();
 
@@ -282,100 +320,189 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     float l_run = 0.0f;
 
     const int gr = tid & 31, gp = tid >> 5;        // gather role: row gr, part gp
-    // score operand: row l32, chunk 36*half + 2ks + g
-    const int qk_off = krow(l32) + 16 * (36 * half + g);
-    // transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
-    // second read of a k-half, +16 for the second k-half), 8 bytes at latent
-    // dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
-    const int tr_off = krow(4 * g + ((lane >> 2) & 3)) + 2 * (256 * half + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
+    // per-lane offsets inside a K tile:
+    //  score operand: row l32, chunk 36*half + 2ks + g
+    const uint32_t qk_off = krow(l32) + 16 * (36 * half + g);
+    //  transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
+    //  second read of a k-half, +16 for the second k-half), 8 bytes at latent
+    //  dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
+    const uint32_t tr_off = krow(4 * g + ((lane >> 2) & 3)) + 2 * (256 * half + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    //  dequantized row gr, part gp: 8 latent chunks and one rope chunk
+    const uint32_t dq_off = krow(gr) + 128 * gp;
+    const uint32_t rope_off = krow(gr) + 16 * (64 + gp);
+    const uint32_t kb0 = lds_addr(lds);
+    // exchange buffers: wavefront w's partial of register group q4 for lane l
+    // at (w*4 + q4)*64 + l (16 bytes each); buffer xb at xb * kXBytes
+    const uint32_t x_own = pin(kb0 + kKBufs * kKTileBytes + wave * 4096 + 16 * lane);
+    const uint32_t x_partner = pin(kb0 + kKBufs * kKTileBytes + (wave ^ 1) * 4096 + 16 * lane);
 
-    // One tile: scores from buffer tt&1 while rows of tile tt+1 (held in nxt)
-    // are dequantized into the other buffer and rows of tile tt+3 are
-    // requested into nxt; then softmax and P.V.
-    auto tile_step = [&](int tt, int n_t, RowPart &nxt) {
-        const uint8_t *kcur = lds + (tt & 1) * kKTileBytes;
-        const uint64_t vmask = __ballot(lane < kTile && slots[tt * kTile + lane] >= 0);
+    // partial scores S^T over this half's 288 dims for the K tile at sb (=
+    // tile + qk_off), written to exchange buffer xb (one accumulator chain;
+    // fp32 queries add their lo parts into the same chain)
+    auto scores_to_x = [&](uint32_t sb, int xb) {
         floatx16_t sacc = {};
-        if (group_live) {
-            if constexpr (QF32) {
 #pragma unroll
-                for (int ks = 0; ks < 18; ++ks) {
-                    const half8_t a = *reinterpret_cast<const half8_t *>(kcur + qk_off + 32 * ks);
-                    sacc = mfma32(a, qb[ks], sacc);
-                    sacc = mfma32(a, ql[ks], sacc);
-                    if (ks % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bound the read-ahead window
-                }
-            } else {
-                floatx16_t s2 = {};
+        for (int ks = 0; ks < 18; ++ks) {
+            const half8_t a = lds_ld<half8_t>(sb + 32 * ks);
+            sacc = mfma32(a, qb[ks], sacc);
+            if constexpr (QF32) sacc = mfma32(a, ql[ks], sacc);
+        }
 #pragma unroll
-                for (int ks = 0; ks < 18; ++ks) {
-                    const half8_t a = *reinterpret_cast<const half8_t *>(kcur + qk_off + 32 * ks);
-                    if (ks & 1) s2 = mfma32(a, qb[ks], s2);
-                    else sacc = mfma32(a, qb[ks], sacc);
-                }
-                sacc += s2;
+        for (int q4 = 0; q4 < 4; ++q4)
+            lds_st<floatx4_t>(x_own + xb * kXBytes + 1024 * q4,
+                              floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
+    };
+
+    // P of tile t from exchange buffer xb: own + partner partial scores,
+    // P = 2^(s - m_ref) as the two fp16 B operands of P.V; updates l_run (the
+    // sum of the fp16 P that P.V uses), m_ref, m_max.  The chunk's last tile
+    // takes the masked form, where the padding rows' scores become -inf.
+    half8_t pb0 = {}, pb1 = {};
+    bool need_redo = false;
+    int last_rows = kTile;                             // valid rows of the chunk's last tile
+    // O^T[256 x 32] += V^T P^T for the K tile at tb (= tile + tr_off), V^T
+    // through transposing reads.  The lane's base row is 0..7 (shift 0 or 1),
+    // so row base + d (d = 0, 8, 16, 24) starts krow(d) bytes further on.
+    auto pv = [&](uint32_t tb) {
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const short4_t lo = lds_read_tr16(tb + krow(16 * kk) + 64 * md);
+                const short4_t hi = lds_read_tr16(tb + krow(16 * kk + 8) + 64 * md);
+                const half8_t a = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
             }
         }
-        if (tt + 1 < n_t) dequant_part(lds + ((tt + 1) & 1) * kKTileBytes, gr, gp, nxt);
-        if (tt + 3 < n_t) gather_part(p.pool, slots[(tt + 3) * kTile + gr], gp, nxt);
-        if (group_live) {
+    };
+
+    // Steady state, iteration t (one barrier), laid out by hand: the
+    // scheduler is fenced (sched_barrier) after every MFMA slot so that
+    // operand reads stay a few MFMAs ahead and the VALU work sits between the
+    // MFMAs.  Slots 0..17 (36 for fp32 queries): the scores of tile t+1 (K
+    // tile at bB, into exchange buffer xb^1) with the softmax of tile t
+    // (buffer xb) spread over them.  Slots 0..15 of the second loop: P.V of
+    // tile t (bA) with the dequantization of tile t+2 (rows held in cur, into
+    // bC) and then the gather of tile t+4 into cur.  Past the chunk's end the
+    // scores, dequant and gather work on stale buffers nobody reads (the
+    // gather index is clamped to a real tile).
+    auto iteration = [&](auto masked, int t, int n_t, RowPart &cur, uint32_t bA, uint32_t bB, uint32_t bC, int xb) {
+        constexpr int kAhead = 4;                     // score operand reads in flight
+        constexpr int kTrAhead = 3;                   // P.V operand pairs in flight
+        const uint32_t sb = pin(bB + qk_off), tb = pin(bA + tr_off);
+        const uint32_t dq = pin(bC + dq_off), rq = pin(bC + rope_off);
+        const int32_t next_slot = slots[min(t + 4, n_t - 1) * kTile + gr];
+        floatx4_t xo[4], xq[4];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                xbuf[(wave * 4 + q4) * 64 + lane] = floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+        for (int q4 = 0; q4 < 4; ++q4) {
+            xo[q4] = lds_ld<floatx4_t>(x_own + xb * kXBytes + 1024 * q4);
+            xq[q4] = lds_ld<floatx4_t>(x_partner + xb * kXBytes + 1024 * q4);
         }
-        __syncthreads();                           // partial scores and the next tile visible
-        if (group_live) {
+        half8_t ka[kAhead];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const floatx4_t o4 = xbuf[((wave ^ 1) * 4 + q4) * 64 + lane];
-                sacc[4 * q4] += o4[0];
-                sacc[4 * q4 + 1] += o4[1];
-                sacc[4 * q4 + 2] += o4[2];
-                sacc[4 * q4 + 3] += o4[3];
+        for (int i = 0; i < kAhead; ++i) ka[i] = lds_ld<half8_t>(sb + 32 * i);
+        __builtin_amdgcn_sched_barrier(0);
+
+        float raw[16];
+        float rmax = 0.0f, nmr = 0.0f, l0 = 0.0f, l1 = 0.0f;
+        const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        floatx16_t sacc = {};
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+            sacc = mfma32(ka[ks % kAhead], qb[ks], sacc);
+            if constexpr (QF32) sacc = mfma32(ka[ks % kAhead], ql[ks], sacc);
+            if (ks + kAhead < 18) ka[ks % kAhead] = lds_ld<half8_t>(sb + 32 * (ks + kAhead));
+            // softmax of tile t, a piece per slot
+            if (ks == 1 || ks == 2) {                 // own + partner partial scores
+#pragma unroll
+                for (int q4 = 2 * (ks - 1); q4 < 2 * ks; ++q4)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) raw[4 * q4 + i] = xo[q4][i] + xq[q4][i];
             }
-            // ---- softmax numerators.  Register v holds row 8(v/4) + 4g + v%4.
-            float sc16[16];
+            if (ks == 3) {
+                if constexpr (decltype(masked)::value) {   // the chunk's last tile: rows >= last_rows are padding
+                    const int lim = last_rows - 4 * g;      // register v holds row 8(v/4) + 4g + v%4
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sc16[v] = sacc[v] * score_mul;
-            if ((uint32_t)vmask != 0xFFFFFFFFu) {      // a tile with skipped entries
+                    for (int v = 0; v < 16; ++v)
+                        if (8 * (v >> 2) + (v & 3) >= lim) raw[v] = -__builtin_inff();
+                }
+                rmax = __builtin_fmaxf(__builtin_fmaxf(raw[0], raw[1]), raw[2]);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 8 * (v >> 2) + 4 * g + (v & 3);
-                    if (!((vmask >> row) & 1)) sc16[v] = -__builtin_inff();
+                for (int v = 3; v < 15; v += 2) rmax = __builtin_fmaxf(__builtin_fmaxf(rmax, raw[v]), raw[v + 1]);
+                rmax = __builtin_fmaxf(rmax, raw[15]);
+            }
+            if (ks == 4) {
+                // lanes l and l ^ 32 hold the same head
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+                const float tmax = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_mul;
+                m_max = __builtin_fmaxf(m_max, tmax);
+                if (m_ref == -__builtin_inff()) m_ref = tmax;    // first tile with a valid entry
+                need_redo |= tmax > m_ref + kRefSlack;           // P could overflow fp16 (pass 0 only)
+                nmr = m_ref == -__builtin_inff() ? 0.0f : -m_ref;   // nothing valid so far
+            }
+            if (ks >= 5 && ks < 13) {                 // P = 2^(s - m_ref), two per slot; exp2(-inf) = 0
+#pragma unroll
+                for (int v = 2 * (ks - 5); v < 2 * (ks - 4); ++v) {
+                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(raw[v], score_mul, nmr));
+                    if (v < 8) pb0[v] = ph;
+                    else pb1[v - 8] = ph;
                 }
             }
-            float tmax = sc16[0];
+            if (ks == 13 || ks == 14) {               // l += the fp16 P that P.V uses
+                const int i0 = 2 * (ks - 13);
 #pragma unroll
-            for (int v = 1; v < 16; ++v) tmax = __builtin_fmaxf(tmax, sc16[v]);
-            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-            m_max = __builtin_fmaxf(m_max, tmax);
-            if (m_ref == -__builtin_inff()) m_ref = tmax;    // first tile with a valid entry
-            if (tmax > m_ref + kRefSlack) *redo = 1;         // P could overflow fp16 (pass 0 only)
-            half8_t pb0, pb1;
-            float lsum = 0.0f;
-            const float mr = m_ref == -__builtin_inff() ? 0.0f : m_ref;   // nothing valid so far
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float pv = __builtin_amdgcn_exp2f(sc16[v] - mr);   // exp2(-inf) = 0
-                lsum += pv;
-                if (v < 8) pb0[v] = (_Float16)pv;
-                else pb1[v - 8] = (_Float16)pv;
-            }
-            l_run += lsum;
-            // ---- O^T[256 x 32] += V^T P^T, V^T through transposing reads
-#pragma unroll
-            for (int md = 0; md < 8; ++md) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const short4_t lo = lds_read_tr16(kcur, tr_off + kKRowBytes * (16 * kk) + 64 * md);
-                    const short4_t hi = lds_read_tr16(kcur, tr_off + kKRowBytes * (16 * kk + 8) + 64 * md);
-                    const half8_t a = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
+                for (int i = i0; i < i0 + 2; ++i) {
+                    l0 = __builtin_amdgcn_fdot2(half2_t{pb0[2 * i], pb0[2 * i + 1]}, one2, l0, false);
+                    l1 = __builtin_amdgcn_fdot2(half2_t{pb1[2 * i], pb1[2 * i + 1]}, one2, l1, false);
                 }
-                if constexpr (QF32) __builtin_amdgcn_sched_barrier(0);
             }
+            if (ks == 15) l_run += l0 + l1;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();                           // this tile's buffer and the partial scores are free
+
+        // P.V of tile t with the dequantization of tile t+2
+        short4_t tlo[kTrAhead], thi[kTrAhead];
+        auto tr_issue = [&](int j, int slot) {
+            const int md = j >> 1, kk = j & 1;
+            tlo[slot] = lds_read_tr16(tb + krow(16 * kk) + 64 * md);
+            thi[slot] = lds_read_tr16(tb + krow(16 * kk + 8) + 64 * md);
+        };
+#pragma unroll
+        for (int j = 0; j < kTrAhead; ++j) tr_issue(j, j);
+        __builtin_amdgcn_sched_barrier(0);
+        half2_t d[4];
+        const uint32_t cw[8] = {cur.c0[0], cur.c0[1], cur.c0[2], cur.c0[3], cur.c1[0], cur.c1[1], cur.c1[2], cur.c1[3]};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int md = j >> 1, kk = j & 1;
+            const half8_t a = __builtin_bit_cast(
+                half8_t, __builtin_shufflevector(tlo[j % kTrAhead], thi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+            o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
+            if (j + kTrAhead < 16) tr_issue(j + kTrAhead, j % kTrAhead);
+            if (j == 0) block_scales_half_cvt(cur.valid ? cur.sc : 0u, d);
+            if (j >= 1 && j <= 8) {                   // latent chunk j-1 of this lane's part
+                uint32_t v[4];
+                e2m1x8_to_half_cvt(cw[j - 1], d[(j - 1) >> 1], v);
+                lds_st<u32x4_t>(dq + 16 * (j - 1), u32x4_t{v[0], v[1], v[2], v[3]});
+            }
+            if (j == 3) {                             // the scores of tile t+1 to the exchange buffer
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    lds_st<floatx4_t>(x_own + (xb ^ 1) * kXBytes + 1024 * q4,
+                                      floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
+            }
+            if (j == 9) {                             // rope chunk
+                const u32x2_t rp = cur.valid ? cur.rp : u32x2_t{0, 0};
+                uint32_t h[4];
+                e4m3x4_to_half_cvt(rp[0], h);
+                e4m3x4_to_half_cvt(rp[1], h + 2);
+                lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
+            }
+            if (j == 10) gather_part(p.pool, stand_in, next_slot, gp, cur);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
     };
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -385,24 +512,48 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
         if (pass == 1) m_ref = m_max;              // the exact maximum: no P can exceed 1
         for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
             const int c_hi = min(e_hi, c_lo + kSlotCap);
-            const int n_t = (c_hi - c_lo + kTile - 1) / kTile;
             if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) {
                 __syncthreads();                   // slots of the previous chunk are no longer read
                 load_positions(c_lo, c_hi);
                 load_pages();
-                write_slots(n_t * kTile);
+                nv = write_slots();
                 __syncthreads();
             }
-            RowPart ra, rb;
-            gather_part(p.pool, slots[gr], gp, ra);
-            if (n_t > 1) gather_part(p.pool, slots[kTile + gr], gp, rb);
-            dequant_part(lds, gr, gp, ra);
-            if (n_t > 2) gather_part(p.pool, slots[2 * kTile + gr], gp, ra);
-            __syncthreads();                       // tile 0 in buffer 0
-            for (int tt = 0; tt < n_t; tt += 2) {
-                tile_step(tt, n_t, rb);            // rb: tile tt+1 -> buffer, then tile tt+3
-                if (tt + 1 < n_t) tile_step(tt + 1, n_t, ra);   // ra: tile tt+2 -> buffer, then tile tt+4
+            const int n_t = (nv + kTile - 1) / kTile;
+            if (n_t == 0) continue;                // nothing valid in this chunk (uniform)
+            last_rows = nv - kTile * (n_t - 1);
+            // prologue: tiles 0 and 1 into buffers 0 and 1, tiles 2 and 3 in
+            // flight in registers, scores of tile 0
+            uint32_t bA = kb0, bB = kb0 + kKTileBytes, bC = kb0 + 2 * kKTileBytes;
+            RowPart r0, r1;
+            gather_part(p.pool, stand_in, slots[gr], gp, r0);
+            gather_part(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
+            dequant_part(pin(bA + dq_off), pin(bA + rope_off), r0);
+            gather_part(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, r0);
+            dequant_part(pin(bB + dq_off), pin(bB + rope_off), r1);
+            gather_part(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, r1);
+            __syncthreads();                       // tiles 0 and 1 in LDS
+            scores_to_x(pin(bA + qk_off), 0);
+            __syncthreads();
+            // full tiles two at a time, then the last one or two with the
+            // last tile masked
+            int t = 0;
+            for (; t + 2 < n_t; t += 2) {
+                iteration(std::false_type{}, t, n_t, r0, bA, bB, bC, 0);       // r0: tile t+2 -> LDS, then t+4
+                iteration(std::false_type{}, t + 1, n_t, r1, bB, bC, bA, 1);   // r1: tile t+3 -> LDS, then t+5
+                const uint32_t a0 = bA;            // tiles t+2, t+3, t+4 go to bC, bA, bB
+                bA = bC;
+                bC = bB;
+                bB = a0;
             }
+            if (t + 1 < n_t) {
+                iteration(std::false_type{}, t, n_t, r0, bA, bB, bC, 0);
+                iteration(std::true_type{}, t + 1, n_t, r1, bB, bC, bA, 1);
+            } else {
+                iteration(std::true_type{}, t, n_t, r0, bA, bB, bC, 0);
+            }
+            if (need_redo) *redo = 1;
+            __syncthreads();                       // buffers free for the next chunk or pass
         }
         if (pass == 1 || *redo == 0) break;        // uniform: read after the last barrier
     }
