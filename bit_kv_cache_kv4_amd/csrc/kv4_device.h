@@ -143,6 +143,17 @@ __device__ __forceinline__ half2_t block_scale_half(uint32_t code) {
     return half2_t{f, f};
 }
 
+// Four E4M3 block scales (bytes of w) as four fp16 pairs {d_i, d_i}, with the
+// FP8 -> fp16 conversion at scale 1 (exact for every code).
+__device__ __forceinline__ void block_scales_half_cvt(uint32_t w, half2_t d[4]) {
+    const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    d[0] = __builtin_shufflevector(lo, lo, 0, 0);
+    d[1] = __builtin_shufflevector(lo, lo, 1, 1);
+    d[2] = __builtin_shufflevector(hi, hi, 0, 0);
+    d[3] = __builtin_shufflevector(hi, hi, 1, 1);
+}
+
 // One row's 16-byte code chunk (latent dims 32c..32c+31) and its two block
 // scales (bytes of `scales16`) -> 16 fp16 pairs in dim order.
 __device__ __forceinline__ void dequant_chunk(u32x4_t codes, uint32_t scales16, uint32_t out[16]) {
