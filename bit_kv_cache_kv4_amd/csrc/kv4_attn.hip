@@ -44,30 +44,30 @@
 namespace kv4 {
 
 constexpr int kTile = 32;                              // list entries per tile
-constexpr int kKChunks = 76;                           // 16-byte chunks per K-tile row: 72 + shift
-constexpr int kKRowBytes = kKChunks * 16;              // 1216
-constexpr int kKTileBytes = kTile * kKRowBytes;        // 38912
+constexpr int kKChunkBytes = 576;                      // one 16-byte chunk of the 32 rows + 4 slots
+constexpr int kKTileBytes = 72 * kKChunkBytes;         // 41472
 constexpr int kXBytes = 4 * 64 * 16 * 4;               // partial scores: 4 wavefronts x 64 lanes x 16
 constexpr int kSlotCap = 1024;                         // entries translated per chunk
 constexpr int kKBufs = 3;                              // K tiles in flight: P.V(t), scores(t+1), dequant(t+2)
 constexpr int kSlotOff = kKBufs * kKTileBytes + 2 * kXBytes + 16;
 constexpr int kCountOff = kSlotOff + kSlotCap * 4;   // valid entries per (batch, wavefront) of a chunk
-constexpr int kLdsBytes = kCountOff + 64;             // 153680
+constexpr int kQmaxOff = kCountOff + 64;              // per-head query maxima of each wavefront
+constexpr int kLdsBytes = kQmaxOff + 4 * 32 * 4;      // 161872
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// K-tile layout for gfx950's LDS (64 banks of 4 bytes, 256 bytes a clock):
-// row r starts at r * 1216 + 16 * ((r >> 2) & 3).  In 16-byte slots modulo
-// 256 bytes that is 12r + (r >> 2) mod 16, so rows 0..15 (and 16..31) sit in
-// 16 distinct slots: the score reads and the dequantizing writes (16 rows per
-// 16 lanes) are conflict-free.  Rows 4m..4m+3 sit in slots congruent modulo
-// 4, so their 64-byte spans in a transposing read (4 rows x 64 bytes per 32
-// lanes) tile the 256 bytes.  Every address is a per-lane base plus a
-// compile-time offset.
-__host__ __device__ constexpr int krow(int r) { return r * kKRowBytes + 16 * ((r >> 2) & 3); }
-static_assert(krow(kTile - 1) + 2 * kDim <= kKTileBytes, "K-tile rows overlap");
+// K-tile layout, chunk-major: element (row r, dim d) is at
+// (d / 8) * 576 + 16 r + 2 (d % 8), i.e. the 32 rows' copies of one 16-byte
+// chunk are contiguous, padded to 36 slots.  A score operand read (one chunk of
+// 32 rows per 32 lanes) and a dequantizing write (one chunk per 32 lanes) each
+// touch 512 contiguous bytes; a transposing read (4 rows x 4 chunks per 32
+// lanes) touches four 64-byte pieces whose 16-byte slots modulo 256 bytes are
+// 4q + 4g + j, all distinct because 36 = 4 mod 16.  gfx950's LDS serves each
+// at its full rate (256 bytes a clock for reads, 128 for writes) with no bank
+// conflict, and every address is a per-lane base plus a compile-time offset.
+constexpr int kcb(int chunk) { return chunk * kKChunkBytes; }
 
 __device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -116,7 +116,8 @@ __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, co
     R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
 }
 
-// dq = K-tile row base + 128 * part (latent chunks), rq = row base + 16 * (64 + part)
+// dq = the lane's row in its part's first latent chunk (chunk 8 * part), rq =
+// the lane's row in its rope chunk (chunk 64 + part)
 __device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const RowPart &R) {
     const uint32_t sc = R.valid ? R.sc : 0u;
     const u32x2_t rp = R.valid ? R.rp : u32x2_t{0, 0};
@@ -127,7 +128,7 @@ __device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const Row
     for (int i = 0; i < 8; ++i) {
         uint32_t v[4];
         e2m1x8_to_half_cvt(c[i], d[i >> 1], v);
-        lds_st<u32x4_t>(dq + 16 * i, u32x4_t{v[0], v[1], v[2], v[3]});
+        lds_st<u32x4_t>(dq + kcb(i), u32x4_t{v[0], v[1], v[2], v[3]});
     }
     uint32_t h[4];
     e4m3x4_to_half_cvt(rp[0], h);
@@ -137,12 +138,24 @@ __device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const Row
 
 constexpr int kPosPerLane = kSlotCap / 256;
 
+// f(integral_constant<int, I>) for I = B .. E-1, each with its index known at
+// compile time (a plain loop this large is not unrolled by the compiler)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <bool QF32>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     int32_t *redo = reinterpret_cast<int32_t *>(lds + kKBufs * kKTileBytes + 2 * kXBytes);
     int32_t *slots = reinterpret_cast<int32_t *>(lds + kSlotOff);
     int32_t *counts = reinterpret_cast<int32_t *>(lds + kCountOff);
+    float *qmx = reinterpret_cast<float *>(lds + kQmaxOff);
+    const uint32_t kb0 = lds_addr(lds);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x, split = blockIdx.y;
@@ -219,84 +232,98 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
         return nv;
     };
 
-    // first chunk's list entries are in flight while the queries load
+    // ---- Prologue, arranged so its memory round trips overlap: the first
+    // chunk's list entries, then this workgroup's queries (coalesced:
+    // consecutive lanes take consecutive 16-byte chunks of a head's row), the
+    // page-table entries once the list is back, the queries staged in LDS (the
+    // K-tile buffers are not in use yet; rows padded so the fragment reads
+    // below are conflict-free), and the slots.  The query fragments are read,
+    // scaled and converted in the first chunk's prologue, while its first
+    // tiles are being gathered.
+    constexpr int kQElem = QF32 ? 4 : 2;
+    constexpr int kQChunks = kDim * kQElem / 16;           // 16-byte chunks per head row
+    constexpr int kQRow = kDim * kQElem + 16;              // staged head row (1168 or 2320 bytes)
+    constexpr int kQPer = 64 * kQChunks / 256;             // chunks per thread
+    static_assert(64 * kQRow <= kSlotOff - 16, "staged queries overlap the slot list");
     const int first_hi = min(e_hi, e_lo + kSlotCap);
-    if (e_lo < e_hi) load_positions(e_lo, first_hi);
+    if (e_lo < e_hi) load_positions(e_lo, first_hi);       // issued first: loads complete in order
     else load_positions(0, 0);
+    {
+        const int h0 = blockIdx.z * 64;
+        const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * kQElem;
+        u32x4_t qc[kQPer];
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) {
+            const int c = tid + 256 * i, hh = c / kQChunks, part = c % kQChunks;
+            qc[i] = u32x4_t{0, 0, 0, 0};
+            if (h0 + hh < p.n_heads)
+                qc[i] = *reinterpret_cast<const u32x4_t *>(qr + (int64_t)(h0 + hh) * p.q_head_stride * kQElem + 16 * part);
+        }
+        if (e_lo < e_hi) load_pages();
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) {
+            const int c = tid + 256 * i, hh = c / kQChunks, part = c % kQChunks;
+            lds_st<u32x4_t>(kb0 + hh * kQRow + 16 * part, qc[i]);
+        }
+    }
+    int nv = e_lo < e_hi ? write_slots() : 0;      // valid entries of the current chunk (holds a barrier)
+    if (tid == 0) *redo = 0;                       // set only in pass 0; read after its last barrier
+    __syncthreads();
 
     // ---- queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head l32,
     // dims 288*half + 16ks + 8g .. +7 for ks = 0..17.  The power-of-two scale
-    // qs puts the head's largest |q| in [2^13, 2^14): exact in fp16.  All of
-    // the head's loads are issued before any is used.
+    // qs puts the head's largest |q| in [2^13, 2^14): exact in fp16 (fp32
+    // queries: a hi and a lo fp16 part).  Run once, with a barrier, by every
+    // thread (the largest |q| of the head's other half comes from the partner
+    // wavefront through LDS).
     half8_t qb[18];
     half8_t ql[QF32 ? 18 : 1];
     float score_mul = 0.0f;
-    {
-        const int64_t hoff = (int64_t)r * p.q_row_stride + (int64_t)head * p.q_head_stride + 8 * g;
+    auto convert_queries = [&]() {
+        const uint32_t qf = kb0 + ((wave >> 1) * 32 + l32) * kQRow + (288 * half + 8 * g) * kQElem;
         float qmax = 0.0f;
         if constexpr (QF32) {
-            const float *qp = reinterpret_cast<const float *>(p.q) + hoff;
-            float4 own[36];
-            float4 other[36];
+            floatx4_t v[36];
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                const int mine = 288 * half + 16 * ks, theirs = 288 * (half ^ 1) + 16 * ks;
-                own[2 * ks] = own[2 * ks + 1] = other[2 * ks] = other[2 * ks + 1] = float4{0, 0, 0, 0};
-                if (head_live) {
-                    own[2 * ks] = *reinterpret_cast<const float4 *>(qp + mine);
-                    own[2 * ks + 1] = *reinterpret_cast<const float4 *>(qp + mine + 4);
-                    other[2 * ks] = *reinterpret_cast<const float4 *>(qp + theirs);
-                    other[2 * ks + 1] = *reinterpret_cast<const float4 *>(qp + theirs + 4);
-                }
+                v[2 * ks] = lds_ld<floatx4_t>(qf + 64 * ks);
+                v[2 * ks + 1] = lds_ld<floatx4_t>(qf + 64 * ks + 16);
             }
-            if (e_lo < e_hi) load_pages();
 #pragma unroll
-            for (int i = 0; i < 36; ++i) {
-                const float4 a = own[i], b = other[i];
-                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)),
-                                                             __builtin_fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))));
-                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)),
-                                                             __builtin_fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
-            }
+            for (int i = 0; i < 36; ++i)
+                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[i][0]), __builtin_fabsf(v[i][1])),
+                                                             __builtin_fmaxf(__builtin_fabsf(v[i][2]), __builtin_fabsf(v[i][3]))));
             qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
+            if (g == 0) qmx[wave * 32 + l32] = qmax;
+            __syncthreads();
+            qmax = __builtin_fmaxf(qmax, qmx[(wave ^ 1) * 32 + l32]);
             int ex = 0;
             if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
             score_mul = p.score_mul / qs;
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
-                const float v[8] = {own[2 * ks].x, own[2 * ks].y, own[2 * ks].z, own[2 * ks].w,
-                                    own[2 * ks + 1].x, own[2 * ks + 1].y, own[2 * ks + 1].z, own[2 * ks + 1].w};
+            for (int ks = 0; ks < 18; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float x = v[e] * qs;
+                    const float x = v[2 * ks + (e >> 2)][e & 3] * qs;
                     const _Float16 hi = (_Float16)x;
                     qb[ks][e] = hi;
                     ql[ks][e] = (_Float16)(x - (float)hi);
                 }
-            }
         } else {
-            const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) + hoff;
-            u32x4_t own[18], other[18];
+            u32x4_t v[18];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
-                own[ks] = other[ks] = u32x4_t{0, 0, 0, 0};
-                if (head_live) {
-                    own[ks] = *reinterpret_cast<const u32x4_t *>(qp + 288 * half + 16 * ks);
-                    other[ks] = *reinterpret_cast<const u32x4_t *>(qp + 288 * (half ^ 1) + 16 * ks);
-                }
-            }
-            if (e_lo < e_hi) load_pages();
+            for (int ks = 0; ks < 18; ++ks) v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(own[ks][c] << 16)),
-                                                                 __builtin_fabsf(__uint_as_float(own[ks][c] & 0xFFFF0000u))));
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(other[ks][c] << 16)),
-                                                                 __builtin_fabsf(__uint_as_float(other[ks][c] & 0xFFFF0000u))));
-                }
+                for (int c = 0; c < 4; ++c)
+                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[ks][c] << 16)),
+                                                                 __builtin_fabsf(__uint_as_float(v[ks][c] & 0xFFFF0000u))));
             qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
+            if (g == 0) qmx[wave * 32 + l32] = qmax;
+            __syncthreads();
+            qmax = __builtin_fmaxf(qmax, qmx[(wave ^ 1) * 32 + l32]);
             int ex = 0;
             if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
@@ -305,14 +332,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             for (int ks = 0; ks < 18; ++ks)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    qb[ks][2 * c] = (_Float16)(__uint_as_float(own[ks][c] << 16) * qs);
-                    qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(own[ks][c] & 0xFFFF0000u) * qs);
+                    qb[ks][2 * c] = (_Float16)(__uint_as_float(v[ks][c] << 16) * qs);
+                    qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[ks][c] & 0xFFFF0000u) * qs);
                 }
         }
-    }
-    int nv = e_lo < e_hi ? write_slots() : 0;      // valid entries of the current chunk
-    if (tid == 0) *redo = 0;                       // set only in pass 0; read after its last barrier
-    __syncthreads();
+    };
 
     floatx16_t o[8];
     float m_ref = -__builtin_inff();   // reference of P = 2^(s - m_ref) for this lane's head
@@ -322,16 +346,16 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     const int gr = tid & 31, gp = tid >> 5;        // gather role: row gr, part gp
     const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
     // per-lane offsets inside a K tile:
-    //  score operand: row l32, chunk 36*half + 2ks + g
-    const uint32_t qk_off = krow(l32) + 16 * (36 * half + g);
+    //  score operand: row l32 of chunk 36*half + 2ks + g
+    const uint32_t qk_off = kcb(36 * half + g) + 16 * l32;
     //  transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
     //  second read of a k-half, +16 for the second k-half), 8 bytes at latent
     //  dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
-    const uint32_t tr_off = krow(4 * g + ((lane >> 2) & 3)) + 2 * (256 * half + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    //  dequantized row gr, part gp: 8 latent chunks and one rope chunk
-    const uint32_t dq_off = krow(gr) + 128 * gp;
-    const uint32_t rope_off = krow(gr) + 16 * (64 + gp);
-    const uint32_t kb0 = lds_addr(lds);
+    const uint32_t tr_off = kcb(32 * half + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
+                            16 * (4 * g + ((lane >> 2) & 3)) + 8 * (lane & 1);
+    //  dequantized row gr, part gp: latent chunks 8gp..8gp+7 and rope chunk 64+gp
+    const uint32_t dq_off = kcb(8 * gp) + 16 * gr;
+    const uint32_t rope_off = kcb(64 + gp) + 16 * gr;
     // exchange buffers: wavefront w's partial of register group q4 for lane l
     // at (w*4 + q4)*64 + l (16 bytes each); buffer xb at xb * kXBytes
     const uint32_t x_own = pin(kb0 + kKBufs * kKTileBytes + wave * 4096 + 16 * lane);
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
         floatx16_t sacc = {};
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) {
-            const half8_t a = lds_ld<half8_t>(sb + 32 * ks);
+            const half8_t a = lds_ld<half8_t>(sb + kcb(2 * ks));
             sacc = mfma32(a, qb[ks], sacc);
             if constexpr (QF32) sacc = mfma32(a, ql[ks], sacc);
         }
@@ -361,32 +385,23 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     half8_t pb0 = {}, pb1 = {};
     bool need_redo = false;
     int last_rows = kTile;                             // valid rows of the chunk's last tile
-    // O^T[256 x 32] += V^T P^T for the K tile at tb (= tile + tr_off), V^T
-    // through transposing reads.  The lane's base row is 0..7 (shift 0 or 1),
-    // so row base + d (d = 0, 8, 16, 24) starts krow(d) bytes further on.
-    auto pv = [&](uint32_t tb) {
-#pragma unroll
-        for (int md = 0; md < 8; ++md) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const short4_t lo = lds_read_tr16(tb + krow(16 * kk) + 64 * md);
-                const short4_t hi = lds_read_tr16(tb + krow(16 * kk + 8) + 64 * md);
-                const half8_t a = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
-            }
-        }
-    };
-
-    // Steady state, iteration t (one barrier), laid out by hand: the
-    // scheduler is fenced (sched_barrier) after every MFMA slot so that
-    // operand reads stay a few MFMAs ahead and the VALU work sits between the
-    // MFMAs.  Slots 0..17 (36 for fp32 queries): the scores of tile t+1 (K
-    // tile at bB, into exchange buffer xb^1) with the softmax of tile t
-    // (buffer xb) spread over them.  Slots 0..15 of the second loop: P.V of
-    // tile t (bA) with the dequantization of tile t+2 (rows held in cur, into
-    // bC) and then the gather of tile t+4 into cur.  Past the chunk's end the
-    // scores, dequant and gather work on stale buffers nobody reads (the
-    // gather index is clamped to a real tile).
+    // Steady state, iteration t (one barrier), laid out by hand as 34 MFMA
+    // slots: 18 score MFMAs of tile t+1 (K tile at bB, into exchange buffer
+    // xb^1; 36 for fp32 queries) then 16 P.V MFMAs of tile t (bA), the first
+    // half of P first.  The scheduler is fenced (sched_barrier) after every
+    // slot, so operand reads stay a few MFMAs ahead and each slot's other
+    // work sits beside its MFMA.  That work is spread evenly because a
+    // wavefront issues in order (a value that is not ready stalls it) and
+    // gfx950's LDS takes writes at about 64 bytes a clock per CU:
+    //  - the softmax of tile t (exchange buffer xb): sums, a max tree, then
+    //    fma -> exp -> fp16 -> row sums, one step per slot;
+    //  - the dequantization of tile t+2 (rows held in cur, into bC): chunk i
+    //    converted in one slot, scaled and stored a slot later, a store every
+    //    four slots, interleaved with the four stores of the new scores;
+    //  - the gather of tile t+4 into cur, each piece as soon as its
+    //    registers are free.
+    // Past the chunk's end the scores, dequant and gather work on stale
+    // buffers nobody reads (the gather index is clamped to a real tile).
     auto iteration = [&](auto masked, int t, int n_t, RowPart &cur, uint32_t bA, uint32_t bB, uint32_t bC, int xb) {
         constexpr int kAhead = 4;                     // score operand reads in flight
         constexpr int kTrAhead = 3;                   // P.V operand pairs in flight
@@ -401,109 +416,172 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
         }
         half8_t ka[kAhead];
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) ka[i] = lds_ld<half8_t>(sb + 32 * i);
+        for (int i = 0; i < kAhead; ++i) ka[i] = lds_ld<half8_t>(sb + kcb(2 * i));
         __builtin_amdgcn_sched_barrier(0);
 
-        float raw[16];
-        float rmax = 0.0f, nmr = 0.0f, l0 = 0.0f, l1 = 0.0f;
+        short4_t tlo[kTrAhead], thi[kTrAhead];
+        auto tr_issue = [&](int j) {                  // P.V MFMA j: k-half kk = j / 8, dims block md = j % 8
+            const int md = j & 7, kk = j >> 3;
+            tlo[j % kTrAhead] = lds_read_tr16(tb + kcb(4 * md) + 16 * (16 * kk));
+            thi[j % kTrAhead] = lds_read_tr16(tb + kcb(4 * md) + 16 * (16 * kk + 8));
+        };
+        float raw[16], mx[7], e[16], ls[4];
+        float tmax = 0.0f, nmr = 0.0f;
+        uint32_t sw0 = 0, sw1 = 0, sc_sel = 0, cv[2][4], rh[4];
+        u32x2_t rp_sel = {0, 0};
+        half2_t d[4];
+        const uint8_t *nrow = stand_in;
+        bool nvalid = false;
         const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        auto cvt_chunk = [&](int i) {                 // E2M1 codes of latent chunk i -> fp16 at scale 1
+            const uint32_t w = i < 4 ? cur.c0[i] : cur.c1[i - 4];
+            cv[i & 1][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+            cv[i & 1][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+            cv[i & 1][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+            cv[i & 1][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+        };
+        auto scale_store = [&](int i) {               // times the block scale, to the K tile
+            const half2_t di = d[i >> 1];
+            lds_st<u32x4_t>(dq + kcb(i), u32x4_t{__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][0]) * di),
+                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][1]) * di),
+                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][2]) * di),
+                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][3]) * di)});
+        };
+        auto x_store = [&](const floatx16_t &sacc, int q4) {   // new scores for the partner
+            lds_st<floatx4_t>(x_own + (xb ^ 1) * kXBytes + 1024 * q4,
+                              floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
+        };
         floatx16_t sacc = {};
+        static_for<0, 34>([&](auto slot) {
+            constexpr int s = decltype(slot)::value;
+            // ---- the MFMA of the slot and the operand reads ahead of it
+            if constexpr (s < 18) {
+                sacc = mfma32(ka[s % kAhead], qb[s], sacc);
+                if constexpr (QF32) sacc = mfma32(ka[s % kAhead], ql[s], sacc);
+                if constexpr (s + kAhead < 18) ka[s % kAhead] = lds_ld<half8_t>(sb + kcb(2 * (s + kAhead)));
+                if constexpr (s >= 18 - kTrAhead) tr_issue(s - (18 - kTrAhead));
+            } else {
+                constexpr int j = s - 18, md = j & 7, kk = j >> 3;
+                const half8_t a = __builtin_bit_cast(
+                    half8_t, __builtin_shufflevector(tlo[j % kTrAhead], thi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+                o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
+                if constexpr (j + kTrAhead < 16) tr_issue(j + kTrAhead);
+            }
+            // ---- softmax of tile t
+            if constexpr (s == 1 || s == 2) {                   // own + partner partial scores
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            sacc = mfma32(ka[ks % kAhead], qb[ks], sacc);
-            if constexpr (QF32) sacc = mfma32(ka[ks % kAhead], ql[ks], sacc);
-            if (ks + kAhead < 18) ka[ks % kAhead] = lds_ld<half8_t>(sb + 32 * (ks + kAhead));
-            // softmax of tile t, a piece per slot
-            if (ks == 1 || ks == 2) {                 // own + partner partial scores
-#pragma unroll
-                for (int q4 = 2 * (ks - 1); q4 < 2 * ks; ++q4)
+                for (int q4 = 2 * (s - 1); q4 < 2 * s; ++q4)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) raw[4 * q4 + i] = xo[q4][i] + xq[q4][i];
             }
-            if (ks == 3) {
+            if constexpr (s == 2) {
                 if constexpr (decltype(masked)::value) {   // the chunk's last tile: rows >= last_rows are padding
                     const int lim = last_rows - 4 * g;      // register v holds row 8(v/4) + 4g + v%4
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
                         if (8 * (v >> 2) + (v & 3) >= lim) raw[v] = -__builtin_inff();
                 }
-                rmax = __builtin_fmaxf(__builtin_fmaxf(raw[0], raw[1]), raw[2]);
-#pragma unroll
-                for (int v = 3; v < 15; v += 2) rmax = __builtin_fmaxf(__builtin_fmaxf(rmax, raw[v]), raw[v + 1]);
-                rmax = __builtin_fmaxf(rmax, raw[15]);
             }
-            if (ks == 4) {
-                // lanes l and l ^ 32 hold the same head
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-                const float tmax = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * score_mul;
+            if constexpr (s == 3) {                             // row maximum as a tree
+#pragma unroll
+                for (int i = 0; i < 5; ++i)
+                    mx[i] = __builtin_fmaxf(__builtin_fmaxf(raw[3 * i], raw[3 * i + 1]), raw[3 * i + 2]);
+            }
+            if constexpr (s == 4) {
+                mx[5] = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), mx[2]);
+                mx[6] = __builtin_fmaxf(__builtin_fmaxf(mx[3], mx[4]), raw[15]);
+            }
+            if constexpr (s == 5) {                             // lanes l and l ^ 32 hold the same head
+                const float rm = __builtin_fmaxf(mx[5], mx[6]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rm), __float_as_uint(rm), false, false);
+                sw0 = sw[0];
+                sw1 = sw[1];
+            }
+            if constexpr (s == 6) tmax = __builtin_fmaxf(__uint_as_float(sw0), __uint_as_float(sw1)) * score_mul;   // score_mul > 0
+            if constexpr (s == 7) {
                 m_max = __builtin_fmaxf(m_max, tmax);
                 if (m_ref == -__builtin_inff()) m_ref = tmax;    // first tile with a valid entry
                 need_redo |= tmax > m_ref + kRefSlack;           // P could overflow fp16 (pass 0 only)
                 nmr = m_ref == -__builtin_inff() ? 0.0f : -m_ref;   // nothing valid so far
             }
-            if (ks >= 5 && ks < 13) {                 // P = 2^(s - m_ref), two per slot; exp2(-inf) = 0
+            if constexpr (s >= 8 && s < 16) {                   // exponent of two values, 2^ of the previous two
+                constexpr int u = s - 8;
+                if constexpr (u > 0) {
+                    e[2 * u - 2] = __builtin_amdgcn_exp2f(e[2 * u - 2]);   // exp2(-inf) = 0
+                    e[2 * u - 1] = __builtin_amdgcn_exp2f(e[2 * u - 1]);
+                }
+                e[2 * u] = __builtin_fmaf(raw[2 * u], score_mul, nmr);
+                e[2 * u + 1] = __builtin_fmaf(raw[2 * u + 1], score_mul, nmr);
+            }
+            if constexpr (s == 16) {
+                e[14] = __builtin_amdgcn_exp2f(e[14]);
+                e[15] = __builtin_amdgcn_exp2f(e[15]);
 #pragma unroll
-                for (int v = 2 * (ks - 5); v < 2 * (ks - 4); ++v) {
-                    const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(raw[v], score_mul, nmr));
-                    if (v < 8) pb0[v] = ph;
-                    else pb1[v - 8] = ph;
+                for (int v = 0; v < 8; ++v) pb0[v] = (_Float16)e[v];
+            }
+            if constexpr (s == 17) {
+#pragma unroll
+                for (int v = 0; v < 8; ++v) pb1[v] = (_Float16)e[8 + v];
+            }
+            if constexpr (s == 18 || s == 19) {                 // l += the fp16 P that P.V uses: four partial sums
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half2_t pp = s == 18 ? half2_t{pb0[2 * i], pb0[2 * i + 1]} : half2_t{pb1[2 * i], pb1[2 * i + 1]};
+                    ls[i] = __builtin_amdgcn_fdot2(pp, one2, s == 18 ? 0.0f : ls[i], false);
                 }
             }
-            if (ks == 13 || ks == 14) {               // l += the fp16 P that P.V uses
-                const int i0 = 2 * (ks - 13);
-#pragma unroll
-                for (int i = i0; i < i0 + 2; ++i) {
-                    l0 = __builtin_amdgcn_fdot2(half2_t{pb0[2 * i], pb0[2 * i + 1]}, one2, l0, false);
-                    l1 = __builtin_amdgcn_fdot2(half2_t{pb1[2 * i], pb1[2 * i + 1]}, one2, l1, false);
-                }
+            if constexpr (s == 20) {
+                ls[0] += ls[1];
+                ls[2] += ls[3];
             }
-            if (ks == 15) l_run += l0 + l1;
+            if constexpr (s == 21) ls[0] += ls[2];
+            if constexpr (s == 22) l_run += ls[0];
+            // ---- dequantization of tile t+2
+            if constexpr (s == 0) {                             // a skipped entry dequantizes to zeros
+                sc_sel = cur.valid ? cur.sc : 0u;
+                rp_sel = cur.valid ? cur.rp : u32x2_t{0, 0};
+                block_scales_half_cvt(sc_sel, d);
+            }
+            constexpr int ci = s >= 1 && (s - 1) % 4 == 0 && (s - 1) / 4 < 8 ? (s - 1) / 4 : -1;
+            constexpr int si = s >= 2 && (s - 2) % 4 == 0 && (s - 2) / 4 < 8 ? (s - 2) / 4 : -1;
+            if constexpr (ci >= 0) cvt_chunk(ci);    // chunk i converted in slot 1 + 4i
+            if constexpr (si >= 0) scale_store(si);  // and stored a slot later
+            if constexpr (s == 31) {
+                e4m3x4_to_half_cvt(rp_sel[0], rh);
+                e4m3x4_to_half_cvt(rp_sel[1], rh + 2);
+            }
+            if constexpr (s == 32) lds_st<u32x4_t>(rq, u32x4_t{rh[0], rh[1], rh[2], rh[3]});
+            // ---- the new scores to the exchange buffer, between the dequant stores
+            if constexpr (s == 20 || s == 24 || s == 28 || s == 33) x_store(sacc, s == 33 ? 3 : (s - 20) / 4);
+            // ---- gather of tile t+4 into cur, piece by piece
+            if constexpr (s == 3) {
+                nvalid = next_slot >= 0;
+                nrow = nvalid ? p.pool + (int64_t)next_slot * kRowBytes : stand_in;
+            }
+            if constexpr (s == 7) {
+                cur.valid = nvalid;
+                cur.sc = *reinterpret_cast<const uint32_t *>(nrow + kScaleOff + 4 * gp);
+            }
+            if constexpr (s == 14) cur.c0 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp);
+            if constexpr (s == 30) cur.c1 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp + 16);
+            if constexpr (s == 32) cur.rp = *reinterpret_cast<const u32x2_t *>(nrow + kRopeOff + 8 * gp);
             __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // P.V of tile t with the dequantization of tile t+2
-        short4_t tlo[kTrAhead], thi[kTrAhead];
-        auto tr_issue = [&](int j, int slot) {
-            const int md = j >> 1, kk = j & 1;
-            tlo[slot] = lds_read_tr16(tb + krow(16 * kk) + 64 * md);
-            thi[slot] = lds_read_tr16(tb + krow(16 * kk + 8) + 64 * md);
-        };
-#pragma unroll
-        for (int j = 0; j < kTrAhead; ++j) tr_issue(j, j);
-        __builtin_amdgcn_sched_barrier(0);
-        half2_t d[4];
-        const uint32_t cw[8] = {cur.c0[0], cur.c0[1], cur.c0[2], cur.c0[3], cur.c1[0], cur.c1[1], cur.c1[2], cur.c1[3]};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int md = j >> 1, kk = j & 1;
-            const half8_t a = __builtin_bit_cast(
-                half8_t, __builtin_shufflevector(tlo[j % kTrAhead], thi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
-            o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
-            if (j + kTrAhead < 16) tr_issue(j + kTrAhead, j % kTrAhead);
-            if (j == 0) block_scales_half_cvt(cur.valid ? cur.sc : 0u, d);
-            if (j >= 1 && j <= 8) {                   // latent chunk j-1 of this lane's part
-                uint32_t v[4];
-                e2m1x8_to_half_cvt(cw[j - 1], d[(j - 1) >> 1], v);
-                lds_st<u32x4_t>(dq + 16 * (j - 1), u32x4_t{v[0], v[1], v[2], v[3]});
-            }
-            if (j == 3) {                             // the scores of tile t+1 to the exchange buffer
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    lds_st<floatx4_t>(x_own + (xb ^ 1) * kXBytes + 1024 * q4,
-                                      floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
-            }
-            if (j == 9) {                             // rope chunk
-                const u32x2_t rp = cur.valid ? cur.rp : u32x2_t{0, 0};
-                uint32_t h[4];
-                e4m3x4_to_half_cvt(rp[0], h);
-                e4m3x4_to_half_cvt(rp[1], h + 2);
-                lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
-            }
-            if (j == 10) gather_part(p.pool, stand_in, next_slot, gp, cur);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         __syncthreads();
     };
+
+    // the first chunk's first two tiles are on their way while the queries
+    // are converted (the staged queries are read before its barrier, so the
+    // tiles may then overwrite them)
+    RowPart r0, r1;
+    {
+        const int n_t0 = (nv + kTile - 1) / kTile;
+        if (n_t0 > 0) {
+            gather_part(p.pool, stand_in, slots[gr], gp, r0);
+            gather_part(p.pool, stand_in, slots[min(1, n_t0 - 1) * kTile + gr], gp, r1);
+        }
+        convert_queries();
+    }
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -525,9 +603,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             // prologue: tiles 0 and 1 into buffers 0 and 1, tiles 2 and 3 in
             // flight in registers, scores of tile 0
             uint32_t bA = kb0, bB = kb0 + kKTileBytes, bC = kb0 + 2 * kKTileBytes;
-            RowPart r0, r1;
-            gather_part(p.pool, stand_in, slots[gr], gp, r0);
-            gather_part(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
+            if (pass == 1 || c_lo != e_lo) {       // the first chunk's were gathered before the passes
+                gather_part(p.pool, stand_in, slots[gr], gp, r0);
+                gather_part(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
+            }
             dequant_part(pin(bA + dq_off), pin(bA + rope_off), r0);
             gather_part(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, r0);
             dequant_part(pin(bB + dq_off), pin(bB + rope_off), r1);
