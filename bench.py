@@ -115,10 +115,13 @@ def prefill_flops(n_rows, n_heads, k):
     return 2.0 * n_rows * n_heads * k * (576 + 512)
 
 
+ATTN_SOURCES = ("kv4_attn.hip", "kv4_device.h", "kv4_launch.h")   # what the attention kernel is built from
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_kv_cache_kv4_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ATTN_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -193,39 +196,67 @@ def main():
     counts = torch.empty((R,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def step(i):
         st = sets[i % len(sets)]
         kv4.quant_write(st["new_rows"], wl["new_slots"], pool)
         kv4.dedup_compact(st["topk"], out_idx=lists, out_count=counts)
-        if ev is not None:
-            ev[0].record(stream)
         if S > 1:
             kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt,
                                           part_o=part_o, part_lse=part_lse)
-            if ev is not None:
-                ev[1].record(stream)
             kv4.merge_states(part_o, part_lse, out=out, lse=lse)
         else:
             kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=1, out=out, lse=lse)
-            if ev is not None:
-                ev[1].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
 
+    # One HIP graph per rotating input set holds a whole step, so the timed
+    # loop measures the GPU, not the launch overhead of four host calls.
+    step(0)
+    torch.cuda.synchronize(dev)
+    graphs = []
+    for i in range(len(sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
     for i in range(args.warmup):
-        step(i)
+        graphs[i % len(graphs)].replay()
     torch.cuda.synchronize(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     print("[bench] timing %d steps (splits=%d)" % (args.steps, S), file=sys.stderr, flush=True)
-    torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        graphs[(args.warmup + i) % len(graphs)].replay()
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # Average launch duration of the split kernel (and of the merge): a graph
+    # of LAUNCHES back-to-back launches replayed REPS times between events on
+    # the stream they run on.
+    LAUNCHES, REPS = 10, 5
+
+    def launch_ms(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(LAUNCHES):
+                fn()
+        g.replay()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(REPS):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / (LAUNCHES * REPS)
+
+    st0 = sets[0]
+    if S > 1:
+        split_ms = launch_ms(lambda: kv4.sparse_mla_decode_partial(st0["q"], pool, lists, spec.sm_scale, S, page_table=pt,
+                                                                   part_o=part_o, part_lse=part_lse))
+        merge_ms = launch_ms(lambda: kv4.merge_states(part_o, part_lse, out=out, lse=lse))
+    else:
+        split_ms = launch_ms(lambda: kv4.sparse_mla_decode(st0["q"], pool, lists, spec.sm_scale, page_table=pt,
+                                                           num_splits=1, out=out, lse=lse))
+        merge_ms = 0.0
 
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
