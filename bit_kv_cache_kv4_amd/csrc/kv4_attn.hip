@@ -640,18 +640,36 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     if (err && p.err_word) atomicOr(p.err_word, err);
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float m_fin = m_ref == -__builtin_inff() ? 0.0f : m_ref;
-    if (!head_live) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float *orow = p.out + (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)head * kLatent;
+    // O^T of this wavefront (256 dims x 32 heads) leaves through LDS, free
+    // since the passes' last barrier: stored straight from the accumulators
+    // every store instruction would touch 32 heads' rows 2 KB apart; from LDS
+    // each one writes 1 KB of one head's row.  Wavefront w's region holds
+    // [32 heads][256 dims + 4 pad] floats (the padding keeps the transposed
+    // writes conflict-free).
+    constexpr int kORow = 256 + 4;
+    const uint32_t oreg = kb0 + wave * (32 * kORow * 4);
+    static_assert(4 * 32 * kORow * 4 <= kSlotOff - 16, "output staging overlaps the slot list");
+    {
+        const uint32_t ow = pin(oreg + (l32 * kORow + 4 * g) * 4);
 #pragma unroll
-    for (int md = 0; md < 8; ++md)
+        for (int md = 0; md < 8; ++md)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = 256 * half + 32 * md + 8 * j + 4 * g;
-            *reinterpret_cast<floatx4_t *>(orow + d) =
-                floatx4_t{o[md][4 * j], o[md][4 * j + 1], o[md][4 * j + 2], o[md][4 * j + 3]} * inv;
+            for (int j = 0; j < 4; ++j)
+                lds_st<floatx4_t>(ow + (32 * md + 8 * j) * 4,
+                                  floatx4_t{o[md][4 * j], o[md][4 * j + 1], o[md][4 * j + 2], o[md][4 * j + 3]} * inv);
+    }
+    __syncthreads();
+    {
+        const uint32_t orr = pin(oreg + 16 * lane);
+        float *ob = p.out + (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + 256 * half + 4 * lane;
+#pragma unroll
+        for (int h = 0; h < 32; ++h) {
+            const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
+            if (hg * 32 + h < p.n_heads) *reinterpret_cast<floatx4_t *>(ob + (int64_t)(hg * 32 + h) * kLatent) = v;
         }
-    if (half == 0 && g == 0 && p.lse) {
+    }
+    if (head_live && half == 0 && g == 0 && p.lse) {
         const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
         p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
     }
