@@ -177,7 +177,7 @@ def run_cpu_baseline(spec, wl, dev):
 def main():
     args = _args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
