@@ -74,15 +74,20 @@ def test_c5_prefill_rows_subset():
 
 # ----------------------------------------------------- equalities of paths
 def test_partial_plus_merge_equals_decode_bitwise():
+    """Decode equals its two exposed halves bit for bit, for several split
+    counts (16 and 17 included) run on one workspace, some twice in a row."""
     spec = W.C2
     pool_d, _ = pools(spec)
     q, topk, pt = to_dev(W.queries(spec)), to_dev(W.topk_lists(spec)), to_dev(W.page_table(spec))
-    for s in (2, 5):
-        out, lse = kv4.sparse_mla_decode(q, pool_d, topk, spec.sm_scale, page_table=pt, num_splits=s)
+    splits = (2, 5, 16, 16, 17, 3, 3)
+    need = max(kv4.sparse_mla_decode_workspace(q, pool_d, topk, s, page_table=pt) for s in splits)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for s in splits:
+        out, lse = kv4.sparse_mla_decode(q, pool_d, topk, spec.sm_scale, page_table=pt, num_splits=s, workspace=ws)
         po, pl = kv4.sparse_mla_decode_partial(q, pool_d, topk, spec.sm_scale, s, page_table=pt)
         o2, l2 = kv4.merge_states(po, pl)
         torch.cuda.synchronize()
-        assert torch.equal(out, o2) and torch.equal(lse, l2)
+        assert torch.equal(out, o2) and torch.equal(lse, l2), "splits=%d" % s
 
 
 def test_prefill_equals_single_split_decode_bitwise():
