@@ -1,7 +1,10 @@
 // Dedup compaction of top-k lists (README "60+ inference optimizations &
 // kernels", section "4-bit KV cache": dedup compaction).
 //
-// One workgroup of 256 lanes per list.  The list is staged through LDS with
+// One workgroup per list, its width chosen by list length and count: 1024
+// lanes when there are too few lists to fill the compute units, else 256 or
+// (for lists of 1025..2048) 512, whose two workgroups per compute unit hide
+// each other's memory waits best.  The list is staged through LDS with
 // coalesced loads; each lane then owns ITEMS consecutive entries.  Every value
 // >= 0 is inserted into an LDS open-addressing table (compare-and-swap on the
 // key, linear probing) whose slot also keeps the smallest list position seen
@@ -15,7 +18,6 @@
 
 namespace kv4 {
 
-constexpr int kDedupThreads = 256;
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 
 // relaxed workgroup-scope LDS atomics: nothing orders one against another
@@ -31,16 +33,16 @@ __device__ __forceinline__ uint32_t dedup_hash(uint32_t v, int log2_table) {
     return (v * 0x9E3779B1u) >> (32 - log2_table);
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kDedupThreads) void dedup_kernel(const int32_t *__restrict__ idx, int32_t k,
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void dedup_kernel(const int32_t *__restrict__ idx, int32_t k,
                                                               int64_t idx_row_stride, int32_t *__restrict__ out_idx,
                                                               int32_t *__restrict__ out_count, int log2_table) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     const int T = 1 << log2_table;
     uint32_t *keys = lds;                    // T keys, then one private dummy slot per thread
-    int32_t *minpos = reinterpret_cast<int32_t *>(lds + T + kDedupThreads);
-    int32_t *stage = reinterpret_cast<int32_t *>(lds + 2 * T + 2 * kDedupThreads);
-    int32_t *wave_tot = stage + ITEMS * kDedupThreads;
+    int32_t *minpos = reinterpret_cast<int32_t *>(lds + T + THREADS);
+    int32_t *stage = reinterpret_cast<int32_t *>(lds + 2 * T + 2 * THREADS);
+    int32_t *wave_tot = stage + ITEMS * THREADS;
     const int tid = threadIdx.x;
     const int64_t list = blockIdx.x;
     const int32_t *src = idx + list * idx_row_stride;
@@ -49,15 +51,15 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_kernel(const int32_t *__r
         int32_t ld[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const int j = tid + kDedupThreads * i;
+            const int j = tid + THREADS * i;
             ld[i] = j < k ? src[j] : -1;
         }
-        for (int i = 4 * tid; i < T; i += 4 * kDedupThreads) {   // T is a multiple of 4 * 256
+        for (int i = 4 * tid; i < T; i += 4 * THREADS) {   // T is a multiple of 4 * THREADS
             *reinterpret_cast<uint4 *>(keys + i) = uint4{kEmpty, kEmpty, kEmpty, kEmpty};
             *reinterpret_cast<int4 *>(minpos + i) = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
         }
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) stage[tid + kDedupThreads * i] = ld[i];
+        for (int i = 0; i < ITEMS; ++i) stage[tid + THREADS * i] = ld[i];
     }
     __syncthreads();
 
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_kernel(const int32_t *__r
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kDedupThreads / 64; ++w) {
+    for (int w = 0; w < THREADS / 64; ++w) {
         const int t = wave_tot[w];
         base += w < wave ? t : 0;
         total += t;
@@ -148,26 +150,26 @@ __global__ __launch_bounds__(kDedupThreads) void dedup_kernel(const int32_t *__r
     __syncthreads();
 
     int32_t *dst = out_idx + list * (int64_t)k;
-    for (int j = tid; j < k; j += kDedupThreads) dst[j] = j < total ? stage[j] : -1;
+    for (int j = tid; j < k; j += THREADS) dst[j] = j < total ? stage[j] : -1;
     if (tid == 0) out_count[list] = total;
 }
 
-template <int ITEMS>
+template <int THREADS, int ITEMS>
 static hipError_t launch_dedup_items(const int32_t *idx, int64_t n_lists, int32_t k, int64_t stride,
                                      int32_t *out_idx, int32_t *out_count, hipStream_t stream) {
-    int log2_table = 10;   // at least 4 * 256 entries (the table is cleared 16 bytes at a time)
-    while ((1 << log2_table) < 4 * k) ++log2_table;   // load factor at most 1/4: short probes
-    const size_t lds = (size_t)(2 * (1 << log2_table) + 2 * kDedupThreads + ITEMS * kDedupThreads + 4) * 4;
+    int log2_table = 10;   // at least 4 * THREADS entries (cleared 16 bytes a lane at a time)
+    while ((1 << log2_table) < 4 * k || (1 << log2_table) < 4 * THREADS) ++log2_table;   // load factor <= 1/4
+    const size_t lds = (size_t)(2 * (1 << log2_table) + 2 * THREADS + ITEMS * THREADS + 4 * (THREADS / 64)) * 4;
     if (lds > 65536) {
         static bool raised = false;   // benign race: every caller sets the same value
         if (!raised) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dedup_kernel<ITEMS>),
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dedup_kernel<THREADS, ITEMS>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
             raised = true;
         }
     }
-    hipLaunchKernelGGL(dedup_kernel<ITEMS>, dim3((unsigned)n_lists), dim3(kDedupThreads), lds, stream, idx, k,
+    hipLaunchKernelGGL((dedup_kernel<THREADS, ITEMS>), dim3((unsigned)n_lists), dim3(THREADS), lds, stream, idx, k,
                        stride, out_idx, out_count, log2_table);
     return hipGetLastError();
 }
@@ -175,11 +177,16 @@ static hipError_t launch_dedup_items(const int32_t *idx, int64_t n_lists, int32_
 hipError_t launch_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride,
                                 int32_t *out_idx, int32_t *out_count, hipStream_t stream) {
     if (n_lists == 0) return hipSuccess;
-    if (k <= 256) return launch_dedup_items<1>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
-    if (k <= 512) return launch_dedup_items<2>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
-    if (k <= 1024) return launch_dedup_items<4>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
-    if (k <= 2048) return launch_dedup_items<8>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
-    return launch_dedup_items<16>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    if (k <= 256) return launch_dedup_items<256, 1>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    if (k <= 512) return launch_dedup_items<256, 2>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    if (n_lists < 256) {   // fewer lists than compute units: four times the lanes per list
+        if (k <= 1024) return launch_dedup_items<1024, 1>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+        if (k <= 2048) return launch_dedup_items<1024, 2>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+        return launch_dedup_items<1024, 4>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    }
+    if (k <= 1024) return launch_dedup_items<256, 4>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    if (k <= 2048) return launch_dedup_items<512, 4>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
+    return launch_dedup_items<256, 16>(idx, n_lists, k, idx_row_stride, out_idx, out_count, stream);
 }
 
 }  // namespace kv4

@@ -128,10 +128,12 @@ def test_dedup_c4_full_size_bit_exact():
     assert (out_d == out_h).all()
 
 
+# 37 lists take the wide (1024-lane) workgroups for k > 512, 300 lists the
+# 256- and 512-lane ones
+@pytest.mark.parametrize("L", [37, 300])
 @pytest.mark.parametrize("k", [1, 2, 5, 64, 255, 256, 257, 511, 512, 1000, 2048, 2051, 3000, 4096])
-def test_dedup_lengths_and_edge_lists(k):
+def test_dedup_lengths_and_edge_lists(k, L):
     g = np.random.default_rng(k)
-    L = 37
     idx = g.integers(-4, max(3, k // 2), size=(L, k)).astype(np.int32)
     idx[0] = -1                                       # all padding
     idx[1] = 7                                        # one value
