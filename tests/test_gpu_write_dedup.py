@@ -69,9 +69,11 @@ def _adversarial_rows():
             r[16 * b + (b % 16)] = a[b] * (1 if b % 2 else -1)
         r[512:] = np.resize(mids, 64) * g.choice([-1, 1], 64)            # rope at E4M3 midpoints
         rows.append(r.astype(np.float32))
-    # E2M1 ties: amax = 6d exactly, other entries at d * {0.25, 0.75, ..., 5} (+- ulps)
+    # E2M1 ties: amax = 6d exactly, other entries at d * {0.25, 0.75, ..., 5}
+    # and up to 8 ulps either side (quotients at and next to every rounding
+    # midpoint, where a quotient formed without dividing could round apart)
     ties = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-    for k in (-1, 0, 1):
+    for k in (-8, -4, -3, -2, -1, 0, 1, 2, 3, 4, 8):
         r = np.zeros(576, np.float32)
         for b in range(32):
             d = np.float32(oracle.e4m3_value(int(g.integers(1, 0x7F))))
@@ -80,6 +82,13 @@ def _adversarial_rows():
             r[16 * b + 1:16 * b + 8] = t.view(np.float32) * g.choice([-1, 1], 7)
             r[16 * b + 8:16 * b + 16] = g.uniform(-6, 6, 8).astype(np.float32) * d
         rows.append(r)
+    # NaN and infinity among ordinary values (a NaN is no block's maximum and
+    # codes as zero; an infinite maximum saturates the scale)
+    r = g.standard_normal(576).astype(np.float32)
+    r[[3, 40, 77, 300, 515, 570]] = np.nan
+    r[[100, 200]] = np.inf
+    r[201] = -np.inf
+    rows.append(r)
     return np.stack(rows).astype(np.float32)
 
 
