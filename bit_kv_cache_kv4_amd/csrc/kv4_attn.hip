@@ -752,19 +752,37 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 
 // ----------------------------------------------------------------- merge
 
+// One 128-thread workgroup per state t; a thread owns 4 dims per 512.  With
+// at most kMergeBatch parts of at most 512 dims (decode's case), the parts' o
+// are loaded before the weights are formed, so their round trip overlaps that
+// of the lse.  With M the largest lse: w_s = exp(lse_s - M) (an empty part
+// weighs 0), W = the w_s summed in part order, o = (the w_s o_s summed in part
+// order) / W, lse = M + ln W; all parts empty gives o = 0, lse = -inf.
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
     __shared__ float w[64];
     __shared__ float stat[2];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int S = p.n_parts;
+    const float *o_t = p.part_o + t * p.dim;                      // part s at s * n_states * dim
+    const int64_t o_stride = p.n_states * (int64_t)p.dim;
+    const bool early = S <= kMergeBatch && p.dim <= 512;          // uniform
+    floatx4_t v[kMergeBatch];
+    if (early && 4 * tid < p.dim) {
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s)
+            if (s < S) v[s] = *reinterpret_cast<const floatx4_t *>(o_t + s * o_stride + 4 * tid);
+    }
     if (tid == 0) {
         float M = -__builtin_inff();
-        for (int s = 0; s < p.n_parts; ++s) M = __builtin_fmaxf(M, p.part_lse[(int64_t)s * p.n_states + t]);
+        for (int s = 0; s < S; ++s) M = __builtin_fmaxf(M, p.part_lse[(int64_t)s * p.n_states + t]);
         stat[0] = M;
     }
     __syncthreads();
     const float M = stat[0];
-    if (M != -__builtin_inff() && tid < p.n_parts) {
+    if (M != -__builtin_inff() && tid < S) {
         const float ls = p.part_lse[(int64_t)tid * p.n_states + t];
         w[tid] = ls == -__builtin_inff() ? 0.0f : expf(ls - M);
     }
@@ -772,7 +790,7 @@ __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
     if (tid == 0) {
         float W = 0.0f;
         if (M != -__builtin_inff())
-            for (int s = 0; s < p.n_parts; ++s) W += w[s];
+            for (int s = 0; s < S; ++s) W += w[s];
         stat[1] = W;
         if (p.lse) p.lse[t] = M == -__builtin_inff() ? M : M + logf(W);
     }
@@ -780,13 +798,28 @@ __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
     const float W = stat[1];
     const float inv = W > 0.0f ? 1.0f / W : 0.0f;
     float *orow = p.out + (t / p.states_per_row) * p.out_row_stride + (t % p.states_per_row) * p.out_col_stride;
+    if (early) {
+        if (4 * tid < p.dim) {
+            floatx4_t acc = {0, 0, 0, 0};
+            if (W > 0.0f) {
+#pragma unroll
+                for (int s = 0; s < kMergeBatch; ++s) {
+                    if (s < S) {
+                        const float ws = w[s];
+                        if (ws != 0.0f) acc += ws * v[s];
+                    }
+                }
+            }
+            *reinterpret_cast<floatx4_t *>(orow + 4 * tid) = acc * inv;
+        }
+        return;
+    }
     for (int d = 4 * tid; d < p.dim; d += 512) {
         floatx4_t acc = {0, 0, 0, 0};
         if (W > 0.0f)
-            for (int s = 0; s < p.n_parts; ++s) {
+            for (int s = 0; s < S; ++s) {
                 const float ws = w[s];
-                if (ws != 0.0f)
-                    acc += ws * *reinterpret_cast<const floatx4_t *>(p.part_o + ((int64_t)s * p.n_states + t) * p.dim + d);
+                if (ws != 0.0f) acc += ws * *reinterpret_cast<const floatx4_t *>(o_t + s * o_stride + d);
             }
         *reinterpret_cast<floatx4_t *>(orow + d) = acc * inv;
     }
