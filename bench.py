@@ -203,8 +203,8 @@ def main():
 
     def step(i):
         st = sets[i % len(sets)]
-        kv4.quant_write(st["new_rows"], wl["new_slots"], pool)
-        kv4.dedup_compact(st["topk"], out_idx=lists, out_count=counts)
+        # the new rows' write and the lists' compaction: one call, one kernel
+        kv4.write_and_dedup(st["new_rows"], wl["new_slots"], pool, st["topk"], out_idx=lists, out_count=counts)
         if S > 1:
             kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt,
                                           part_o=part_o, part_lse=part_lse)
@@ -213,7 +213,7 @@ def main():
             kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=1, out=out, lse=lse)
 
     # One HIP graph per rotating input set holds a whole step, so the timed
-    # loop measures the GPU, not the launch overhead of four host calls.
+    # loop measures the GPU, not the launch overhead of three host calls.
     step(0)
     torch.cuda.synchronize(dev)
     graphs = []

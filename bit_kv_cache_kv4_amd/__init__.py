@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "Kv4Error", "ROW_BYTES", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
     "library_path", "load", "version", "last_error",
-    "quant_write", "dedup_compact", "sparse_mla_decode", "sparse_mla_decode_partial",
+    "quant_write", "dedup_compact", "write_and_dedup", "sparse_mla_decode", "sparse_mla_decode_partial",
     "sparse_mla_decode_splits", "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill",
     "gather_dequant",
 ]
@@ -84,6 +84,7 @@ def load():
     L.kv4_attn_args_size.argtypes, L.kv4_attn_args_size.restype = [], sz
     L.kv4_quant_write.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
     L.kv4_dedup_compact.argtypes = [vp, i64, i32, i64, vp, vp, vp]
+    L.kv4_write_and_dedup.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i32, i64, vp, vp, vp]
     L.kv4_sparse_mla_decode_splits.argtypes, L.kv4_sparse_mla_decode_splits.restype = [pa], i32
     L.kv4_sparse_mla_decode_workspace.argtypes, L.kv4_sparse_mla_decode_workspace.restype = [pa, i32], sz
     L.kv4_sparse_mla_decode.argtypes = [pa, i32, vp, sz, vp]
@@ -136,28 +137,32 @@ def _need(t, name, dtype, device=None):
 
 
 # ------------------------------------------------------------------ write
-def quant_write(kv, slots, pool, err_word=None, stream=None) -> None:
-    """kv4_quant_write: quantize kv[n] (fp32 [N, >=576] rows) into pool[slots[n]]."""
+def _check_write_args(kv, slots, pool, err_word):
     _need(kv, "kv", torch.float32)
     _need(slots, "slots", torch.int32, kv.device)
     _need(pool, "pool", torch.uint8, kv.device)
     if err_word is not None:
         _need(err_word, "err_word", torch.int32, kv.device)
-    if kv.dim() != 2 or kv.stride(1) != 1 or slots.dim() != 1 or slots.stride(0) != 1 or slots.numel() != kv.shape[0]:
+    if kv.dim() != 2 or slots.dim() != 1 or slots.numel() != kv.shape[0] or (
+            kv.shape[0] > 0 and (kv.stride(1) != 1 or slots.stride(0) != 1)):
         raise ValueError("kv must be [N, >=576] with unit inner stride and slots [N] contiguous")
     if kv.shape[1] < DIM:
         raise ValueError("kv rows need at least 576 values")
     if pool.dim() != 2 or pool.shape[1] != ROW_BYTES or not pool.is_contiguous():
         raise ValueError("pool must be a contiguous [n_slots, 352] uint8 tensor")
+
+
+def quant_write(kv, slots, pool, err_word=None, stream=None) -> None:
+    """kv4_quant_write: quantize kv[n] (fp32 [N, >=576] rows) into pool[slots[n]]."""
+    _check_write_args(kv, slots, pool, err_word)
     _check(load().kv4_quant_write(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
                                   _ptr(err_word), _stream(stream, kv.device)))
 
 
 # ------------------------------------------------------------------ dedup
-def dedup_compact(idx, k=None, out_idx=None, out_count=None, stream=None):
-    """kv4_dedup_compact: per list, first occurrences of values >= 0 in order, -1 fill, counts."""
+def _dedup_outputs(idx, k, out_idx, out_count):
     _need(idx, "idx", torch.int32)
-    if idx.dim() != 2 or idx.stride(1) != 1:
+    if idx.dim() != 2 or (idx.shape[0] > 0 and idx.stride(1) != 1):
         raise ValueError("idx must be [n_lists, >=k] with unit inner stride")
     n, k = idx.shape[0], idx.shape[1] if k is None else int(k)
     if out_idx is None:
@@ -168,8 +173,27 @@ def dedup_compact(idx, k=None, out_idx=None, out_count=None, stream=None):
     _need(out_count, "out_count", torch.int32, idx.device)
     if not out_idx.is_contiguous() or tuple(out_idx.shape) != (n, k) or not out_count.is_contiguous():
         raise ValueError("out_idx must be contiguous [n_lists, k], out_count contiguous [n_lists]")
+    return n, k, out_idx, out_count
+
+
+def dedup_compact(idx, k=None, out_idx=None, out_count=None, stream=None):
+    """kv4_dedup_compact: per list, first occurrences of values >= 0 in order, -1 fill, counts."""
+    n, k, out_idx, out_count = _dedup_outputs(idx, k, out_idx, out_count)
     _check(load().kv4_dedup_compact(_ptr(idx), n, k, idx.stride(0), _ptr(out_idx), _ptr(out_count),
                                     _stream(stream, idx.device)))
+    return out_idx, out_count
+
+
+def write_and_dedup(kv, slots, pool, idx, k=None, out_idx=None, out_count=None, err_word=None, stream=None):
+    """kv4_write_and_dedup: quant_write(kv, slots, pool) and dedup_compact(idx) as one call
+    (one kernel with fewer than 256 lists); returns (out_idx, out_count)."""
+    _check_write_args(kv, slots, pool, err_word)
+    if idx.device != kv.device:
+        raise ValueError("idx must be on the device of kv")
+    n, k, out_idx, out_count = _dedup_outputs(idx, k, out_idx, out_count)
+    _check(load().kv4_write_and_dedup(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
+                                      _ptr(err_word), _ptr(idx), n, k, idx.stride(0), _ptr(out_idx),
+                                      _ptr(out_count), _stream(stream, kv.device)))
     return out_idx, out_count
 
 

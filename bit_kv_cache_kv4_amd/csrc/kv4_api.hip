@@ -152,8 +152,12 @@ const char *kv4_last_error(void) { return g_err; }
 
 size_t kv4_attn_args_size(void) { return sizeof(kv4_attn_args); }
 
-kv4_status kv4_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
-                           uint8_t *pool, int64_t n_slots, uint32_t *err_word, void *stream) {
+namespace {
+
+// Argument checks of kv4_quant_write; *work is false when there is nothing to write.
+kv4_status check_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                             const uint8_t *pool, int64_t n_slots, bool *work) {
+    *work = false;
     if (n_tokens < 0) return fail(KV4_ERR_SHAPE, "n_tokens = %lld < 0", (long long)n_tokens);
     if (n_slots < 0) return fail(KV4_ERR_SHAPE, "n_slots = %lld < 0", (long long)n_slots);
     if (n_tokens > (int64_t)4 * 0x7FFFFFFF) return fail(KV4_ERR_UNSUPPORTED, "n_tokens too large");
@@ -165,13 +169,14 @@ kv4_status kv4_quant_write(const float *kv, int64_t kv_row_stride, const int32_t
     if (!aligned(kv, 16)) return fail(KV4_ERR_ALIGN, "kv must be 16-byte aligned");
     if (pool && !aligned(pool, 16)) return fail(KV4_ERR_ALIGN, "pool must be 16-byte aligned");
     if (!aligned(slots, 4)) return fail(KV4_ERR_ALIGN, "slots must be 4-byte aligned");
-    return hip_status(kv4::launch_quant_write(kv, kv_row_stride, slots, n_tokens, pool, pool ? n_slots : 0, err_word,
-                                              (hipStream_t)stream),
-                      "quant_write launch");
+    *work = true;
+    return ok();
 }
 
-kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,
-                             int32_t *out_count, void *stream) {
+// Argument checks of kv4_dedup_compact; *work is false when there is no list.
+kv4_status check_dedup(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride, const int32_t *out_idx,
+                       const int32_t *out_count, bool *work) {
+    *work = false;
     if (n_lists < 0 || k < 0) return fail(KV4_ERR_SHAPE, "n_lists or k < 0");
     if (k > KV4_MAX_DEDUP_K) return fail(KV4_ERR_UNSUPPORTED, "k = %d > %d", k, KV4_MAX_DEDUP_K);
     if (n_lists > 0x7FFFFFFF) return fail(KV4_ERR_UNSUPPORTED, "n_lists too large");
@@ -183,8 +188,60 @@ kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int
         const char *b0 = reinterpret_cast<const char *>(out_idx), *b1 = b0 + 4 * (n_lists * (int64_t)k);
         if (a0 < b1 && b0 < a1) return fail(KV4_ERR_SHAPE, "out_idx overlaps idx");
     }
+    *work = true;
+    return ok();
+}
+
+}  // namespace
+
+kv4_status kv4_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                           uint8_t *pool, int64_t n_slots, uint32_t *err_word, void *stream) {
+    bool work = false;
+    const kv4_status st = check_quant_write(kv, kv_row_stride, slots, n_tokens, pool, n_slots, &work);
+    if (st != KV4_OK || !work) return st;
+    return hip_status(kv4::launch_quant_write(kv, kv_row_stride, slots, n_tokens, pool, pool ? n_slots : 0, err_word,
+                                              (hipStream_t)stream),
+                      "quant_write launch");
+}
+
+kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,
+                             int32_t *out_count, void *stream) {
+    bool work = false;
+    const kv4_status st = check_dedup(idx, n_lists, k, idx_row_stride, out_idx, out_count, &work);
+    if (st != KV4_OK || !work) return st;
     return hip_status(kv4::launch_dedup_compact(idx, n_lists, k, idx_row_stride, out_idx, out_count, (hipStream_t)stream),
                       "dedup_compact launch");
+}
+
+kv4_status kv4_write_and_dedup(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                               uint8_t *pool, int64_t n_slots, uint32_t *err_word, const int32_t *idx,
+                               int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,
+                               int32_t *out_count, void *stream) {
+    bool write = false, dedup = false;
+    kv4_status st = check_quant_write(kv, kv_row_stride, slots, n_tokens, pool, n_slots, &write);
+    if (st != KV4_OK) return st;
+    st = check_dedup(idx, n_lists, k, idx_row_stride, out_idx, out_count, &dedup);
+    if (st != KV4_OK) return st;
+    if (!write && !dedup) return ok();
+    kv4::WriteDedupParams p{};
+    if (write) {
+        p.kv = kv;
+        p.kv_row_stride = kv_row_stride;
+        p.slots = slots;
+        p.n_tokens = n_tokens;
+        p.pool = pool;
+        p.n_slots = pool ? n_slots : 0;
+        p.err_word = err_word;
+    }
+    if (dedup) {
+        p.idx = idx;
+        p.n_lists = n_lists;
+        p.k = k;
+        p.idx_row_stride = idx_row_stride;
+        p.out_idx = out_idx;
+        p.out_count = out_count;
+    }
+    return hip_status(kv4::launch_write_dedup(p, (hipStream_t)stream), "write_and_dedup launch");
 }
 
 int32_t kv4_sparse_mla_decode_splits(const kv4_attn_args *a) {

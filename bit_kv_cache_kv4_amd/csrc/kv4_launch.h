@@ -14,6 +14,27 @@ hipError_t launch_quant_write(const float *kv, int64_t kv_row_stride, const int3
 hipError_t launch_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride,
                                 int32_t *out_idx, int32_t *out_count, hipStream_t stream);
 
+// The row write and the list compaction in one launch (both as above).
+struct WriteDedupParams {
+    const float *kv;
+    int64_t kv_row_stride;
+    const int32_t *slots;
+    int64_t n_tokens;
+    uint8_t *pool;
+    int64_t n_slots;
+    uint32_t *err_word;
+    const int32_t *idx;
+    int64_t n_lists;
+    int32_t k;
+    int64_t idx_row_stride;
+    int32_t *out_idx;
+    int32_t *out_count;
+};
+
+// One kernel when there are fewer lists than compute units (its workgroups
+// hold either a list or 16 rows), else the two launches above.
+hipError_t launch_write_dedup(const WriteDedupParams &p, hipStream_t stream);
+
 struct AttnParams {
     const void *q;
     int64_t q_row_stride, q_head_stride;

@@ -121,6 +121,20 @@ kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int
                              int32_t *out_idx, int32_t *out_count, void *stream);
 
 /*
+ * kv4_quant_write and kv4_dedup_compact in one call, the decode step's work
+ * before attention (README, "4-bit KV cache": the quantized write and the
+ * dedup compaction).  The two are independent; with fewer than 256 lists they
+ * run as one kernel, so there is one launch boundary instead of two and their
+ * memory waits overlap; with more, as the two kernels.  Arguments, results
+ * and errors are exactly those of the two calls (n_tokens == 0 or n_lists == 0
+ * leaves that part out); out_idx must not overlap the pool or kv either.
+ */
+kv4_status kv4_write_and_dedup(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                               uint8_t *pool, int64_t n_slots, uint32_t *err_word, const int32_t *idx,
+                               int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,
+                               int32_t *out_count, void *stream);
+
+/*
  * Arguments of the attention entry points.  For query row r and head h the
  * result is, over the valid entries j of row r's list,
  *   s_j = sm_scale * sum_{i<576} q[r, h, i] * K_j[i]

@@ -147,6 +147,23 @@ def test_dedup_argument_checks():
     assert f(V(0x1000), 4, 16, 16, None, V(0x200000), None) == 1
 
 
+def test_write_and_dedup_argument_checks():
+    """The combined call checks both halves exactly as the two calls do and
+    launches nothing when both are empty (no GPU needed for any of these)."""
+    lib = kv4.load()
+    f = lib.kv4_write_and_dedup
+    V = ctypes.c_void_p
+    w_ok = (V(0x10), 576, V(0x10), 4, V(0x20), 8, None)
+    d_ok = (V(0x100000), 4, 16, 16, V(0x200000), V(0x300000))
+    assert f(None, 576, None, 0, None, 0, None, None, 0, 16, 16, None, None, None) == 0     # nothing to do
+    assert f(None, 576, V(0x10), 4, V(0x20), 8, None, *d_ok, None) == 1                    # write half: kv NULL
+    assert f(V(0x10), 575, V(0x10), 4, V(0x20), 8, None, *d_ok, None) == 3                  # write half: stride
+    assert f(*w_ok, V(0x100000), 4, 4097, 4097, V(0x200000), V(0x300000), None) == 4        # dedup half: k
+    assert f(*w_ok, V(0x1000), 4, 16, 16, V(0x1010), V(0x300000), None) == 2                # dedup half: overlap
+    assert "overlap" in kv4.last_error()
+    assert f(*w_ok, V(0x1000), 4, 16, 16, None, V(0x300000), None) == 1
+
+
 def test_merge_argument_checks():
     lib = kv4.load()
     f = lib.kv4_merge_states

@@ -169,3 +169,56 @@ def test_dedup_empty_calls():
     out, cnt = kv4.dedup_compact(idx)
     torch.cuda.synchronize()
     assert (cnt.cpu() == 0).all()
+
+
+# ------------------------------------------- the write and the compaction in one call
+def _write_and_dedup_both(kv, slots, n_slots, idx, k=None):
+    """The combined call on the GPU against the oracle's write and dedup."""
+    pool_h = np.full((n_slots, 352), 0xA5, np.uint8)
+    err_h = oracle.quant_write(kv, slots, pool_h) if kv.shape[0] else 0
+    out_h, cnt_h = oracle.dedup_compact(idx[:, :k] if k is not None else idx)
+    pool_d = torch.full((n_slots, 352), 0xA5, dtype=torch.uint8, device=DEV)
+    err_d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out_d, cnt_d = kv4.write_and_dedup(to_dev(kv), to_dev(slots), pool_d, to_dev(idx), k=k, err_word=err_d)
+    torch.cuda.synchronize()
+    return (pool_d.cpu().numpy(), pool_h, int(err_d.item()), err_h, out_d.cpu().numpy(), cnt_d.cpu().numpy(),
+            out_h, cnt_h)
+
+
+@pytest.mark.parametrize("n_tokens,n_lists,k", [
+    (64, 64, 2048),      # the decode step: one kernel, lists of 2048
+    (1, 1, 5),
+    (0, 37, 1000),       # compaction only
+    (70, 0, 16),         # write only
+    (33, 5, 4096),       # longest lists
+    (17, 300, 700),      # enough lists for the two separate kernels
+])
+def test_write_and_dedup_equals_oracle(n_tokens, n_lists, k):
+    g = np.random.default_rng(1000 + n_tokens + n_lists + k)
+    kv = (g.standard_normal((n_tokens, 576)) * 2).astype(np.float32)
+    n_slots = 4 * n_tokens + 8
+    slots = g.permutation(n_slots)[:n_tokens].astype(np.int32)
+    if n_tokens > 4:
+        slots[1] = -1                   # pad: nothing written
+        slots[3] = n_slots + 5          # out of range: flagged
+    idx = g.integers(-3, max(3, k // 3), size=(n_lists, k)).astype(np.int32)
+    got, want, e_d, e_h, out_d, cnt_d, out_h, cnt_h = _write_and_dedup_both(kv, slots, n_slots, idx)
+    _assert_same_bytes(got, want)
+    assert e_d == e_h
+    assert (cnt_d == cnt_h).all() and (out_d == out_h).all()
+
+
+def test_write_and_dedup_prefix_k_and_step_inputs():
+    """The decode step's own inputs (the long-context pool's new rows and
+    lists) with a prefix k of a wider list buffer."""
+    spec = W.C3
+    g = np.random.default_rng(11)
+    kv = g.standard_normal((spec.n_req, 576)).astype(np.float32)
+    slots = g.permutation(4096)[:spec.n_req].astype(np.int32)
+    idx = W.topk_lists(spec)
+    wide = np.full((idx.shape[0], idx.shape[1] + 64), -7, np.int32)
+    wide[:, :idx.shape[1]] = idx
+    got, want, e_d, e_h, out_d, cnt_d, out_h, cnt_h = _write_and_dedup_both(kv, slots, 4096, wide, k=idx.shape[1])
+    _assert_same_bytes(got, want)
+    assert e_d == e_h == 0
+    assert (cnt_d == cnt_h).all() and (out_d == out_h).all()
