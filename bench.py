@@ -212,26 +212,48 @@ def main():
         else:
             kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=1, out=out, lse=lse)
 
-    # One HIP graph per rotating input set holds a whole step, so the timed
-    # loop measures the GPU, not the launch overhead of three host calls.
+    # The timed steps run from HIP graphs that hold one step per rotating
+    # input set, in order (a step's three calls are launched by the GPU, not
+    # by the host), as they would sit inside a model's decode graph; a
+    # remainder graph completes K.  For comparison, the same K steps with one
+    # graph launch per step, whose host launch gap (~8 us) falls between
+    # every two steps.
     step(0)
     torch.cuda.synchronize(dev)
-    graphs = []
-    for i in range(len(sets)):
+    n_sets = len(sets)
+
+    def capture(first, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(i)
-        graphs.append(g)
+            for i in range(count):
+                step(first + i)
+        return g
+
+    per_step = [capture(i, 1) for i in range(n_sets)]
+    full = capture(0, n_sets)
+
+    def run_steps(k):
+        for _ in range(k // n_sets):
+            full.replay()
+        if k % n_sets:
+            rest.replay()
+
+    rest = capture(0, args.steps % n_sets) if args.steps % n_sets else None
     for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+        per_step[i % n_sets].replay()
+    full.replay()                        # the multi-step graph's first replay, untimed
     torch.cuda.synchronize(dev)
     print("[bench] timing %d steps (splits=%d)" % (args.steps, S), file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % len(graphs)].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        per_step[i % n_sets].replay()
+    torch.cuda.synchronize(dev)
+    per_step_ms = (time.perf_counter() - t2) / args.steps * 1e3
 
     # Average launch duration of the split kernel (and of the merge): a graph
     # of LAUNCHES back-to-back launches replayed REPS times between events on
@@ -297,6 +319,7 @@ def main():
                      "mfma_tflops": round(decode_flops / (split_ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(decode_flops / (split_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "merge_avg_launch_ms": round(merge_ms, 5),
+        "ms_per_step_one_graph_per_step": round(per_step_ms, 5),
         "decode_gbs_incl_merge": round(algo / ((split_ms + merge_ms) * 1e-3) / 1e9, 1),
     }
 
