@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = [
-    "Kv4Error", "ROW_BYTES", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
+    "Kv4Error", "ROW_BYTES", "ROW_BYTES_ROPE_FREE", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
     "library_path", "load", "version", "last_error",
     "quant_write", "dedup_compact", "write_and_dedup", "sparse_mla_decode", "sparse_mla_decode_partial",
     "sparse_mla_decode_splits", "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill",
@@ -28,9 +28,11 @@ __all__ = [
 ]
 
 LATENT, ROPE, DIM, ROW_BYTES = 512, 64, 576, 352
+ROW_BYTES_ROPE_FREE = 288           # the rope-free row: codes and block scales only
 ERRBIT_PAGE, ERRBIT_SLOT = 1, 2
 MAX_DEDUP_K, MAX_SPLITS = 4096, 64
 _F32, _BF16 = 0, 1
+_ROW_ROPE, _ROW_ROPE_FREE = 0, 1
 _STATUS = {0: "KV4_OK", 1: "KV4_ERR_NULL", 2: "KV4_ERR_SHAPE", 3: "KV4_ERR_ALIGN", 4: "KV4_ERR_UNSUPPORTED",
            5: "KV4_ERR_WORKSPACE", 6: "KV4_ERR_HIP"}
 
@@ -61,6 +63,7 @@ class AttnArgs(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p), ("out_row_stride", ctypes.c_int64),
         ("lse", ctypes.c_void_p), ("err_word", ctypes.c_void_p),
+        ("row_format", ctypes.c_int32),
     ]
 
 
@@ -83,6 +86,7 @@ def load():
     L.kv4_last_error.argtypes, L.kv4_last_error.restype = [], ctypes.c_char_p
     L.kv4_attn_args_size.argtypes, L.kv4_attn_args_size.restype = [], sz
     L.kv4_quant_write.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
+    L.kv4_quant_write_rope_free.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
     L.kv4_dedup_compact.argtypes = [vp, i64, i32, i64, vp, vp, vp]
     L.kv4_write_and_dedup.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i32, i64, vp, vp, vp]
     L.kv4_sparse_mla_decode_splits.argtypes, L.kv4_sparse_mla_decode_splits.restype = [pa], i32
@@ -137,7 +141,7 @@ def _need(t, name, dtype, device=None):
 
 
 # ------------------------------------------------------------------ write
-def _check_write_args(kv, slots, pool, err_word):
+def _check_write_args(kv, slots, pool, err_word, rope_free=False):
     _need(kv, "kv", torch.float32)
     _need(slots, "slots", torch.int32, kv.device)
     _need(pool, "pool", torch.uint8, kv.device)
@@ -146,14 +150,21 @@ def _check_write_args(kv, slots, pool, err_word):
     if kv.dim() != 2 or slots.dim() != 1 or slots.numel() != kv.shape[0] or (
             kv.shape[0] > 0 and (kv.stride(1) != 1 or slots.stride(0) != 1)):
         raise ValueError("kv must be [N, >=576] with unit inner stride and slots [N] contiguous")
-    if kv.shape[1] < DIM:
-        raise ValueError("kv rows need at least 576 values")
-    if pool.dim() != 2 or pool.shape[1] != ROW_BYTES or not pool.is_contiguous():
-        raise ValueError("pool must be a contiguous [n_slots, 352] uint8 tensor")
+    dim, row = (LATENT, ROW_BYTES_ROPE_FREE) if rope_free else (DIM, ROW_BYTES)
+    if kv.shape[1] < dim:
+        raise ValueError("kv rows need at least %d values" % dim)
+    if pool.dim() != 2 or pool.shape[1] != row or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous [n_slots, %d] uint8 tensor" % row)
 
 
 def quant_write(kv, slots, pool, err_word=None, stream=None) -> None:
-    """kv4_quant_write: quantize kv[n] (fp32 [N, >=576] rows) into pool[slots[n]]."""
+    """kv4_quant_write: quantize kv[n] (fp32 [N, >=576] rows) into pool[slots[n]]; with a
+    rope-free pool ([n_slots, 288]) kv4_quant_write_rope_free of fp32 [N, >=512] rows."""
+    if pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE:
+        _check_write_args(kv, slots, pool, err_word, rope_free=True)
+        _check(load().kv4_quant_write_rope_free(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool),
+                                                pool.shape[0], _ptr(err_word), _stream(stream, kv.device)))
+        return
     _check_write_args(kv, slots, pool, err_word)
     _check(load().kv4_quant_write(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
                                   _ptr(err_word), _stream(stream, kv.device)))
@@ -205,10 +216,15 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
     dev = q.device
     _need(pool, "pool", torch.uint8, dev)
     _need(topk, "topk", torch.int32, dev)
-    if q.dim() != 3 or q.shape[2] != DIM or q.stride(2) != 1:
-        raise ValueError("q must be [n_rows, n_heads, 576] with unit inner stride")
-    if pool.dim() != 2 or pool.shape[1] != ROW_BYTES or not pool.is_contiguous():
-        raise ValueError("pool must be a contiguous [n_slots, 352] uint8 tensor")
+    # the pool's row width names the format: 352-byte rows (q of 576 dims) or
+    # 288-byte rope-free rows (q of 512)
+    if pool.dim() != 2 or pool.shape[1] not in (ROW_BYTES, ROW_BYTES_ROPE_FREE) or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous [n_slots, 352] or [n_slots, 288] uint8 tensor")
+    rope_free = pool.shape[1] == ROW_BYTES_ROPE_FREE
+    dim = LATENT if rope_free else DIM
+    if q.dim() != 3 or q.shape[2] != dim or q.stride(2) != 1:
+        raise ValueError("q must be [n_rows, n_heads, %d] with unit inner stride for a %d-byte pool"
+                         % (dim, pool.shape[1]))
     if topk.dim() != 2 or topk.stride(1) != 1 or topk.shape[0] != q.shape[0]:
         raise ValueError("topk must be [n_rows, k] with unit inner stride")
     a = AttnArgs()
@@ -217,6 +233,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
     a.q, a.q_row_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
     a.n_rows, a.n_heads = q.shape[0], q.shape[1]
     a.pool, a.n_slots = pool.data_ptr(), pool.shape[0]
+    a.row_format = _ROW_ROPE_FREE if rope_free else _ROW_ROPE
     if page_table is not None:
         _need(page_table, "page_table", torch.int32, dev)
         if page_table.dim() != 2 or page_table.stride(1) != 1:
@@ -337,11 +354,13 @@ def sparse_mla_prefill(q, pool, topk, sm_scale, page_table=None, row_req=None, p
 
 
 def gather_dequant(pool, topk, page_table=None, row_req=None, page_size=64, err_word=None, stream=None):
-    """kv4_gather_dequant; returns (rows [R, k, 576] float16, slots [R, k] int32)."""
+    """kv4_gather_dequant; returns (rows [R, k, D] float16, slots [R, k] int32), D = 576, or 512
+    for a rope-free (288-byte) pool."""
     R, k = topk.shape[0], topk.shape[1]
-    dummy_q = torch.empty((R, 16, DIM), dtype=torch.bfloat16, device=topk.device)
+    dim = LATENT if pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE else DIM
+    dummy_q = torch.empty((R, 16, dim), dtype=torch.bfloat16, device=topk.device)
     a = _attn_args(dummy_q, pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
-    out = torch.empty((R, k, DIM), dtype=torch.float16, device=topk.device)
+    out = torch.empty((R, k, dim), dtype=torch.float16, device=topk.device)
     slots = torch.empty((R, k), dtype=torch.int32, device=topk.device)
     _check(load().kv4_gather_dequant(ctypes.byref(a), _ptr(out), _ptr(slots), _stream(stream, topk.device)))
     return out, slots

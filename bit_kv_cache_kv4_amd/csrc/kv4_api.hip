@@ -49,6 +49,8 @@ kv4_status check_attn(const kv4_attn_args *a, bool need_out) {
         return fail(KV4_ERR_SHAPE, "args->struct_size = %u, this library expects %zu", a->struct_size,
                     sizeof(kv4_attn_args));
     if (a->q_dtype != KV4_BF16 && a->q_dtype != KV4_F32) return fail(KV4_ERR_SHAPE, "q_dtype must be KV4_BF16 or KV4_F32");
+    if (a->row_format != KV4_ROW_ROPE && a->row_format != KV4_ROW_ROPE_FREE)
+        return fail(KV4_ERR_SHAPE, "row_format must be KV4_ROW_ROPE or KV4_ROW_ROPE_FREE");
     if (a->n_rows < 0) return fail(KV4_ERR_SHAPE, "n_rows = %d < 0", a->n_rows);
     if (a->n_heads < 16 || a->n_heads > 128 || a->n_heads % 16)
         return fail(KV4_ERR_UNSUPPORTED, "n_heads = %d; supported: a multiple of 16 in [16, 128]", a->n_heads);
@@ -61,9 +63,10 @@ kv4_status check_attn(const kv4_attn_args *a, bool need_out) {
     if (need_out && !a->out) return fail(KV4_ERR_NULL, "out is NULL");
     const int64_t vec = a->q_dtype == KV4_BF16 ? 8 : 4;
     if (!aligned(a->q, 16)) return fail(KV4_ERR_ALIGN, "q must be 16-byte aligned");
-    if (a->q_head_stride < KV4_DIM || a->q_head_stride % vec)
-        return fail(KV4_ERR_ALIGN, "q_head_stride = %lld; need >= 576 and a multiple of %lld", (long long)a->q_head_stride,
-                    (long long)vec);
+    const int64_t dim = a->row_format == KV4_ROW_ROPE_FREE ? KV4_LATENT : KV4_DIM;
+    if (a->q_head_stride < dim || a->q_head_stride % vec)
+        return fail(KV4_ERR_ALIGN, "q_head_stride = %lld; need >= %lld and a multiple of %lld", (long long)a->q_head_stride,
+                    (long long)dim, (long long)vec);
     if (a->q_row_stride < 0 || a->q_row_stride % vec || (a->n_rows > 1 && a->q_row_stride < a->q_head_stride * a->n_heads))
         return fail(KV4_ERR_ALIGN, "q_row_stride = %lld; need >= n_heads * q_head_stride and a multiple of %lld",
                     (long long)a->q_row_stride, (long long)vec);
@@ -113,6 +116,7 @@ kv4::AttnParams base_params(const kv4_attn_args *a) {
     p.k = a->k;
     p.score_mul = a->sm_scale * 1.44269504088896340736f;
     p.err_word = a->err_word;
+    p.rope_dims = a->row_format == KV4_ROW_ROPE_FREE ? 0 : KV4_ROPE;
     return p;
 }
 
@@ -156,7 +160,7 @@ namespace {
 
 // Argument checks of kv4_quant_write; *work is false when there is nothing to write.
 kv4_status check_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
-                             const uint8_t *pool, int64_t n_slots, bool *work) {
+                             const uint8_t *pool, int64_t n_slots, bool *work, int64_t dim = KV4_DIM) {
     *work = false;
     if (n_tokens < 0) return fail(KV4_ERR_SHAPE, "n_tokens = %lld < 0", (long long)n_tokens);
     if (n_slots < 0) return fail(KV4_ERR_SHAPE, "n_slots = %lld < 0", (long long)n_slots);
@@ -164,8 +168,9 @@ kv4_status check_quant_write(const float *kv, int64_t kv_row_stride, const int32
     if (n_tokens == 0) return ok();
     if (!kv || !slots) return fail(KV4_ERR_NULL, "kv or slots is NULL");
     if (!pool && n_slots > 0) return fail(KV4_ERR_NULL, "pool is NULL");
-    if (kv_row_stride < KV4_DIM || kv_row_stride % 4)
-        return fail(KV4_ERR_ALIGN, "kv_row_stride = %lld; need >= 576 and a multiple of 4", (long long)kv_row_stride);
+    if (kv_row_stride < dim || kv_row_stride % 4)
+        return fail(KV4_ERR_ALIGN, "kv_row_stride = %lld; need >= %lld and a multiple of 4", (long long)kv_row_stride,
+                    (long long)dim);
     if (!aligned(kv, 16)) return fail(KV4_ERR_ALIGN, "kv must be 16-byte aligned");
     if (pool && !aligned(pool, 16)) return fail(KV4_ERR_ALIGN, "pool must be 16-byte aligned");
     if (!aligned(slots, 4)) return fail(KV4_ERR_ALIGN, "slots must be 4-byte aligned");
@@ -202,6 +207,16 @@ kv4_status kv4_quant_write(const float *kv, int64_t kv_row_stride, const int32_t
     return hip_status(kv4::launch_quant_write(kv, kv_row_stride, slots, n_tokens, pool, pool ? n_slots : 0, err_word,
                                               (hipStream_t)stream),
                       "quant_write launch");
+}
+
+kv4_status kv4_quant_write_rope_free(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                                     uint8_t *pool, int64_t n_slots, uint32_t *err_word, void *stream) {
+    bool work = false;
+    const kv4_status st = check_quant_write(kv, kv_row_stride, slots, n_tokens, pool, n_slots, &work, KV4_LATENT);
+    if (st != KV4_OK || !work) return st;
+    return hip_status(kv4::launch_quant_write_rope_free(kv, kv_row_stride, slots, n_tokens, pool, pool ? n_slots : 0,
+                                                        err_word, (hipStream_t)stream),
+                      "quant_write_rope_free launch");
 }
 
 kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,

@@ -36,6 +36,13 @@
 //      block.
 // The per-split result is written normalised with its lse; a split count of 1
 // writes the final output.
+//
+// Rows are either the 352-byte format (576 dims: 512 latent + 64 rope) or the
+// 288-byte rope-free format (512 latent dims; README, "4-bit KV cache": the
+// rope-free row of GLM-5.3-Flash).  The rope-free kernel is the same with 16
+// score k-steps per half instead of 18 and no rope to gather or decode; it
+// keeps the same slot schedule and LDS layout (the last 8 chunks of each K
+// tile unused).
 #include "kv4_device.h"
 #include "kv4_launch.h"
 
@@ -106,18 +113,27 @@ struct RowPart {
 // A skipped entry reads 352 readable bytes elsewhere (`stand_in`: the query
 // row, at least 1152 bytes, so an empty pool is never touched) and is zeroed by
 // dequant_part: scale and rope bytes become 0, so every value is 0.
+// Row layout: 352 bytes with the 64 rope values, or the 288-byte rope-free
+// row (codes and scales only, README "60+ inference optimizations & kernels",
+// section "4-bit KV cache": GLM-5.3-Flash's rope-free row).
+template <bool ROPE>
+constexpr int row_bytes() { return ROPE ? kRowBytes : kScaleOff + kLatent / 16; }
+
+template <bool ROPE>
 __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, const uint8_t *stand_in, int32_t slot,
                                             int gp, RowPart &R) {
     R.valid = slot >= 0;
-    const uint8_t *row = R.valid ? pool + (int64_t)slot * kRowBytes : stand_in;
+    const uint8_t *row = R.valid ? pool + (int64_t)slot * row_bytes<ROPE>() : stand_in;
     R.c0 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp);
     R.c1 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp + 16);
     R.sc = *reinterpret_cast<const uint32_t *>(row + kScaleOff + 4 * gp);
-    R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
+    if constexpr (ROPE) R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
+    else R.rp = u32x2_t{0, 0};
 }
 
 // dq = the lane's row in its part's first latent chunk (chunk 8 * part), rq =
 // the lane's row in its rope chunk (chunk 64 + part)
+template <bool ROPE>
 __device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const RowPart &R) {
     const uint32_t sc = R.valid ? R.sc : 0u;
     const u32x2_t rp = R.valid ? R.rp : u32x2_t{0, 0};
@@ -130,10 +146,12 @@ __device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const Row
         e2m1x8_to_half_cvt(c[i], d[i >> 1], v);
         lds_st<u32x4_t>(dq + kcb(i), u32x4_t{v[0], v[1], v[2], v[3]});
     }
-    uint32_t h[4];
-    e4m3x4_to_half_cvt(rp[0], h);
-    e4m3x4_to_half_cvt(rp[1], h + 2);
-    lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
+    if constexpr (ROPE) {
+        uint32_t h[4];
+        e4m3x4_to_half_cvt(rp[0], h);
+        e4m3x4_to_half_cvt(rp[1], h + 2);
+        lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
+    }
 }
 
 constexpr int kPosPerLane = kSlotCap / 256;
@@ -148,8 +166,14 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-template <bool QF32>
+template <bool QF32, bool ROPE>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
+    // row format: K has kD dims (latent + rope, or latent only); each half of
+    // the scores covers kD / 2 of them in kSteps MFMA k-steps of 16
+    constexpr int kD = ROPE ? kDim : kLatent;
+    constexpr int kSteps = kD / 32;
+    constexpr int kHalfChunks = kD / 16;
+    constexpr int kRowB = row_bytes<ROPE>();
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     int32_t *redo = reinterpret_cast<int32_t *>(lds + kKBufs * kKTileBytes + 2 * kXBytes);
     int32_t *slots = reinterpret_cast<int32_t *>(lds + kSlotOff);
@@ -241,8 +265,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     // scaled and converted in the first chunk's prologue, while its first
     // tiles are being gathered.
     constexpr int kQElem = QF32 ? 4 : 2;
-    constexpr int kQChunks = kDim * kQElem / 16;           // 16-byte chunks per head row
-    constexpr int kQRow = kDim * kQElem + 16;              // staged head row (1168 or 2320 bytes)
+    constexpr int kQChunks = kD * kQElem / 16;             // 16-byte chunks per head row
+    constexpr int kQRow = kD * kQElem + 16;                // staged head row (at most 2320 bytes)
     constexpr int kQPer = 64 * kQChunks / 256;             // chunks per thread
     static_assert(64 * kQRow <= kSlotOff - 16, "staged queries overlap the slot list");
     const int first_hi = min(e_hi, e_lo + kSlotCap);
@@ -276,21 +300,21 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     // queries: a hi and a lo fp16 part).  Run once, with a barrier, by every
     // thread (the largest |q| of the head's other half comes from the partner
     // wavefront through LDS).
-    half8_t qb[18];
-    half8_t ql[QF32 ? 18 : 1];
+    half8_t qb[kSteps];
+    half8_t ql[QF32 ? kSteps : 1];
     float score_mul = 0.0f;
     auto convert_queries = [&]() {
-        const uint32_t qf = kb0 + ((wave >> 1) * 32 + l32) * kQRow + (288 * half + 8 * g) * kQElem;
+        const uint32_t qf = kb0 + ((wave >> 1) * 32 + l32) * kQRow + (kD / 2 * half + 8 * g) * kQElem;
         float qmax = 0.0f;
         if constexpr (QF32) {
-            floatx4_t v[36];
+            floatx4_t v[2 * kSteps];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
+            for (int ks = 0; ks < kSteps; ++ks) {
                 v[2 * ks] = lds_ld<floatx4_t>(qf + 64 * ks);
                 v[2 * ks + 1] = lds_ld<floatx4_t>(qf + 64 * ks + 16);
             }
 #pragma unroll
-            for (int i = 0; i < 36; ++i)
+            for (int i = 0; i < 2 * kSteps; ++i)
                 qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[i][0]), __builtin_fabsf(v[i][1])),
                                                              __builtin_fmaxf(__builtin_fabsf(v[i][2]), __builtin_fabsf(v[i][3]))));
             qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
             score_mul = p.score_mul / qs;
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks)
+            for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = v[2 * ks + (e >> 2)][e & 3] * qs;
@@ -311,11 +335,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
                     ql[ks][e] = (_Float16)(x - (float)hi);
                 }
         } else {
-            u32x4_t v[18];
+            u32x4_t v[kSteps];
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
+            for (int ks = 0; ks < kSteps; ++ks) v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks)
+            for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[ks][c] << 16)),
@@ -329,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
             score_mul = p.score_mul / qs;
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks)
+            for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     qb[ks][2 * c] = (_Float16)(__uint_as_float(v[ks][c] << 16) * qs);
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
     // per-lane offsets inside a K tile:
     //  score operand: row l32 of chunk 36*half + 2ks + g
-    const uint32_t qk_off = kcb(36 * half + g) + 16 * l32;
+    const uint32_t qk_off = kcb(kHalfChunks * half + g) + 16 * l32;
     //  transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
     //  second read of a k-half, +16 for the second k-half), 8 bytes at latent
     //  dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     auto scores_to_x = [&](uint32_t sb, int xb) {
         floatx16_t sacc = {};
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
+        for (int ks = 0; ks < kSteps; ++ks) {
             const half8_t a = lds_ld<half8_t>(sb + kcb(2 * ks));
             sacc = mfma32(a, qb[ks], sacc);
             if constexpr (QF32) sacc = mfma32(a, ql[ks], sacc);
@@ -452,21 +476,24 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
                               floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
         };
         floatx16_t sacc = {};
+        // The softmax of tile t delivers P in slots 16 and 17, so P.V starts at
+        // slot 18 in both row formats; the rope-free scores take slots 0..15
+        // and leave 16 and 17 without an MFMA.
         static_for<0, 34>([&](auto slot) {
             constexpr int s = decltype(slot)::value;
             // ---- the MFMA of the slot and the operand reads ahead of it
-            if constexpr (s < 18) {
+            if constexpr (s < kSteps) {
                 sacc = mfma32(ka[s % kAhead], qb[s], sacc);
                 if constexpr (QF32) sacc = mfma32(ka[s % kAhead], ql[s], sacc);
-                if constexpr (s + kAhead < 18) ka[s % kAhead] = lds_ld<half8_t>(sb + kcb(2 * (s + kAhead)));
-                if constexpr (s >= 18 - kTrAhead) tr_issue(s - (18 - kTrAhead));
-            } else {
+                if constexpr (s + kAhead < kSteps) ka[s % kAhead] = lds_ld<half8_t>(sb + kcb(2 * (s + kAhead)));
+            } else if constexpr (s >= 18) {
                 constexpr int j = s - 18, md = j & 7, kk = j >> 3;
                 const half8_t a = __builtin_bit_cast(
                     half8_t, __builtin_shufflevector(tlo[j % kTrAhead], thi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
                 o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
                 if constexpr (j + kTrAhead < 16) tr_issue(j + kTrAhead);
             }
+            if constexpr (s >= 18 - kTrAhead && s < 18) tr_issue(s - (18 - kTrAhead));
             // ---- softmax of tile t
             if constexpr (s == 1 || s == 2) {                   // own + partner partial scores
 #pragma unroll
@@ -546,17 +573,17 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             constexpr int si = s >= 2 && (s - 2) % 4 == 0 && (s - 2) / 4 < 8 ? (s - 2) / 4 : -1;
             if constexpr (ci >= 0) cvt_chunk(ci);    // chunk i converted in slot 1 + 4i
             if constexpr (si >= 0) scale_store(si);  // and stored a slot later
-            if constexpr (s == 31) {
+            if constexpr (ROPE && s == 31) {
                 e4m3x4_to_half_cvt(rp_sel[0], rh);
                 e4m3x4_to_half_cvt(rp_sel[1], rh + 2);
             }
-            if constexpr (s == 32) lds_st<u32x4_t>(rq, u32x4_t{rh[0], rh[1], rh[2], rh[3]});
+            if constexpr (ROPE && s == 32) lds_st<u32x4_t>(rq, u32x4_t{rh[0], rh[1], rh[2], rh[3]});
             // ---- the new scores to the exchange buffer, between the dequant stores
             if constexpr (s == 20 || s == 24 || s == 28 || s == 33) x_store(sacc, s == 33 ? 3 : (s - 20) / 4);
             // ---- gather of tile t+4 into cur, piece by piece
             if constexpr (s == 3) {
                 nvalid = next_slot >= 0;
-                nrow = nvalid ? p.pool + (int64_t)next_slot * kRowBytes : stand_in;
+                nrow = nvalid ? p.pool + (int64_t)next_slot * kRowB : stand_in;
             }
             if constexpr (s == 7) {
                 cur.valid = nvalid;
@@ -564,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             }
             if constexpr (s == 14) cur.c0 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp);
             if constexpr (s == 30) cur.c1 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp + 16);
-            if constexpr (s == 32) cur.rp = *reinterpret_cast<const u32x2_t *>(nrow + kRopeOff + 8 * gp);
+            if constexpr (ROPE && s == 32) cur.rp = *reinterpret_cast<const u32x2_t *>(nrow + kRopeOff + 8 * gp);
             __builtin_amdgcn_sched_barrier(0);
         });
         __syncthreads();
@@ -577,8 +604,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     {
         const int n_t0 = (nv + kTile - 1) / kTile;
         if (n_t0 > 0) {
-            gather_part(p.pool, stand_in, slots[gr], gp, r0);
-            gather_part(p.pool, stand_in, slots[min(1, n_t0 - 1) * kTile + gr], gp, r1);
+            gather_part<ROPE>(p.pool, stand_in, slots[gr], gp, r0);
+            gather_part<ROPE>(p.pool, stand_in, slots[min(1, n_t0 - 1) * kTile + gr], gp, r1);
         }
         convert_queries();
     }
@@ -604,13 +631,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
             // flight in registers, scores of tile 0
             uint32_t bA = kb0, bB = kb0 + kKTileBytes, bC = kb0 + 2 * kKTileBytes;
             if (pass == 1 || c_lo != e_lo) {       // the first chunk's were gathered before the passes
-                gather_part(p.pool, stand_in, slots[gr], gp, r0);
-                gather_part(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
+                gather_part<ROPE>(p.pool, stand_in, slots[gr], gp, r0);
+                gather_part<ROPE>(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
             }
-            dequant_part(pin(bA + dq_off), pin(bA + rope_off), r0);
-            gather_part(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, r0);
-            dequant_part(pin(bB + dq_off), pin(bB + rope_off), r1);
-            gather_part(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, r1);
+            dequant_part<ROPE>(pin(bA + dq_off), pin(bA + rope_off), r0);
+            gather_part<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, r0);
+            dequant_part<ROPE>(pin(bB + dq_off), pin(bB + rope_off), r1);
+            gather_part<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, r1);
             __syncthreads();                       // tiles 0 and 1 in LDS
             scores_to_x(pin(bA + qk_off), 0);
             __syncthreads();
@@ -678,15 +705,21 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
 hipError_t launch_sparse_mla(const AttnParams &p, bool q_f32, int32_t n_splits, hipStream_t stream) {
     if (p.n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)p.n_rows, (unsigned)n_splits, (unsigned)((p.n_heads + 63) / 64));
-    if (q_f32) hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, dim3(256), 0, stream, p);
+    if (p.rope_dims == kRope) {
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
 // --------------------------------------------------- dequantizing gather
 
 // One workgroup per (query row, tile of 32 entries): translate, then the same
-// lane roles and decoding as the attention kernel, written row-major to HBM.
+// lane roles and decoding as the attention kernel, written row-major to HBM
+// (576 fp16 values per entry, or 512 for rope-free rows).
 __global__ __launch_bounds__(256) void gather_dequant_kernel(AttnParams p, uint16_t *__restrict__ out,
                                                              int32_t *__restrict__ slots_out) {
     __shared__ int32_t slots[kTile];
@@ -708,6 +741,8 @@ __global__ __launch_bounds__(256) void gather_dequant_kernel(AttnParams p, uint1
         if (err && p.err_word) atomicOr(p.err_word, err);
     }
     __syncthreads();
+    const bool rope = p.rope_dims == kRope;
+    const int row_b = rope ? kRowBytes : kScaleOff + kLatent / 16, dim = rope ? kDim : kLatent;
     const int pp = tid & 15, qc = tid >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -717,18 +752,18 @@ __global__ __launch_bounds__(256) void gather_dequant_kernel(AttnParams p, uint1
         u32x4_t codes = {0, 0, 0, 0};
         uint32_t sc = 0;
         if (s >= 0) {
-            const uint8_t *src = p.pool + (int64_t)s * kRowBytes;
+            const uint8_t *src = p.pool + (int64_t)s * row_b;
             codes = *reinterpret_cast<const u32x4_t *>(src + 16 * qc);
             sc = *reinterpret_cast<const uint16_t *>(src + kScaleOff + 2 * qc);
         }
         uint32_t v[16];
         dequant_chunk(codes, sc, v);
-        uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * kDim) + 16 * qc;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * dim) + 16 * qc;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             *reinterpret_cast<u32x4_t *>(dst + 4 * c) = u32x4_t{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
     }
-    if (tid < 128) {
+    if (rope && tid < 128) {
         const int row = tid >> 2, e = tile * kTile + row;
         if (e < p.k) {
             const int32_t s = slots[row];
@@ -736,7 +771,7 @@ __global__ __launch_bounds__(256) void gather_dequant_kernel(AttnParams p, uint1
             if (s >= 0) b = *reinterpret_cast<const u32x4_t *>(p.pool + (int64_t)s * kRowBytes + kRopeOff + 16 * (tid & 3));
             uint32_t h[8];
             dequant_rope16(b, h);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * kDim) + kLatent / 2 + 8 * (tid & 3);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * dim) + kLatent / 2 + 8 * (tid & 3);
             *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{h[0], h[1], h[2], h[3]};
             *reinterpret_cast<u32x4_t *>(dst + 4) = u32x4_t{h[4], h[5], h[6], h[7]};
         }

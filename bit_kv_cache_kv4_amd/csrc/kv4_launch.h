@@ -11,6 +11,11 @@ hipError_t launch_quant_write(const float *kv, int64_t kv_row_stride, const int3
                               int64_t n_tokens, uint8_t *pool, int64_t n_slots, uint32_t *err_word,
                               hipStream_t stream);
 
+// the same for the 288-byte rope-free row (kv rows of 512 values)
+hipError_t launch_quant_write_rope_free(const float *kv, int64_t kv_row_stride, const int32_t *slots,
+                                        int64_t n_tokens, uint8_t *pool, int64_t n_slots, uint32_t *err_word,
+                                        hipStream_t stream);
+
 hipError_t launch_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride,
                                 int32_t *out_idx, int32_t *out_count, hipStream_t stream);
 
@@ -55,6 +60,7 @@ struct AttnParams {
     float *lse;                // element (s, r, h) at s*lse_split_stride + r*lse_row_stride + h
     int64_t lse_row_stride, lse_split_stride;
     uint32_t *err_word;
+    int32_t rope_dims;         // 64: 352-byte rows, q of 576 dims; 0: 288-byte rope-free rows, q of 512
 };
 
 // grid = (n_rows, n_splits, ceil(n_heads / 64))

@@ -17,6 +17,23 @@ __global__ __launch_bounds__(256) void quant_write_kernel(const float *__restric
                     (int64_t)blockIdx.x * kQuantRowsPerBlock + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
+__global__ __launch_bounds__(256) void quant_write_rope_free_kernel(const float *__restrict__ kv, int64_t kv_row_stride,
+                                                                    const int32_t *__restrict__ slots, int64_t n_tokens,
+                                                                    uint8_t *__restrict__ pool, int64_t n_slots,
+                                                                    uint32_t *__restrict__ err_word) {
+    quant_write_row<false>(kv, kv_row_stride, slots, n_tokens, pool, n_slots, err_word,
+                           (int64_t)blockIdx.x * kQuantRowsPerBlock + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+hipError_t launch_quant_write_rope_free(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                                        uint8_t *pool, int64_t n_slots, uint32_t *err_word, hipStream_t stream) {
+    if (n_tokens == 0) return hipSuccess;
+    const int64_t blocks = (n_tokens + kQuantRowsPerBlock - 1) / kQuantRowsPerBlock;
+    hipLaunchKernelGGL(quant_write_rope_free_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kv, kv_row_stride,
+                       slots, n_tokens, pool, n_slots, err_word);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
                               uint8_t *pool, int64_t n_slots, uint32_t *err_word, hipStream_t stream) {
     if (n_tokens == 0) return hipSuccess;

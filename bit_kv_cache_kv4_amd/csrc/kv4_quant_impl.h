@@ -38,7 +38,10 @@ __device__ __forceinline__ uint32_t e2m1x8_hw(const float y[8]) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
 }
 
-// Row `row` written by one wavefront (lane = its lane index).
+// Row `row` written by one wavefront (lane = its lane index).  ROPE: the
+// 352-byte row from 576 values; otherwise the 288-byte rope-free row (codes
+// and scales) from 512.
+template <bool ROPE = true>
 __device__ __forceinline__ void quant_write_row(const float *__restrict__ kv, int64_t kv_row_stride,
                                                 const int32_t *__restrict__ slots, int64_t n_tokens,
                                                 uint8_t *__restrict__ pool, int64_t n_slots,
@@ -49,7 +52,7 @@ __device__ __forceinline__ void quant_write_row(const float *__restrict__ kv, in
     const float *src = kv + row * kv_row_stride;
     const float4 v0 = *reinterpret_cast<const float4 *>(src + 8 * lane);
     const float4 v1 = *reinterpret_cast<const float4 *>(src + 8 * lane + 4);
-    const float r = src[kLatent + lane];
+    const float r = ROPE ? src[kLatent + lane] : 0.0f;
     if (slot < 0) return;                        // pad row: writes nothing
     if ((int64_t)slot >= n_slots) {
         if (lane == 0 && err_word) atomicOr(err_word, kErrSlot);
@@ -107,10 +110,10 @@ __device__ __forceinline__ void quant_write_row(const float *__restrict__ kv, in
         packed |= ((is_scale ? t : (t >> 8)) & 0xFFu) << (8 * j);
     }
 
-    uint8_t *dst = pool + (int64_t)slot * kRowBytes;
+    uint8_t *dst = pool + (int64_t)slot * (ROPE ? kRowBytes : kScaleOff + kLatent / 16);
     reinterpret_cast<uint32_t *>(dst)[lane] = word;
     if (lane < 8) reinterpret_cast<uint32_t *>(dst + kScaleOff)[lane] = packed;
-    else if (lane < 24) reinterpret_cast<uint32_t *>(dst + kRopeOff)[lane - 8] = packed;
+    else if (ROPE && lane < 24) reinterpret_cast<uint32_t *>(dst + kRopeOff)[lane - 8] = packed;
 }
 
 }  // namespace kv4

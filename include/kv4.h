@@ -67,6 +67,12 @@ typedef enum {
 
 typedef enum { KV4_F32 = 0, KV4_BF16 = 1 } kv4_dtype;
 
+/* Row formats of the pool (README, "4-bit KV cache"): the 352-byte row with
+ * 64 E4M3 rope values after the codes and scales, and GLM-5.3-Flash's
+ * 288-byte rope-free row (codes and scales only, 512 dims). */
+typedef enum { KV4_ROW_ROPE = 0, KV4_ROW_ROPE_FREE = 1 } kv4_row_format;
+#define KV4_ROW_BYTES_ROPE_FREE 288
+
 #define KV4_ERRBIT_PAGE 1u /* position past the page table, or page entry < 0 */
 #define KV4_ERRBIT_SLOT 2u /* slot >= n_slots */
 
@@ -104,6 +110,16 @@ kv4_status kv4_quant_write(const float *kv, int64_t kv_row_stride, const int32_t
                            void *stream);
 
 /*
+ * kv4_quant_write for the 288-byte rope-free row (README, "4-bit KV cache":
+ * GLM-5.3-Flash's rope-free row): kv rows hold the 512 latent values
+ * (kv_row_stride >= 512), pool is [n_slots, 288] (codes [0, 256), block
+ * scales [256, 288)).  Everything else as kv4_quant_write.
+ */
+kv4_status kv4_quant_write_rope_free(const float *kv, int64_t kv_row_stride, const int32_t *slots,
+                                     int64_t n_tokens, uint8_t *pool, int64_t n_slots, uint32_t *err_word,
+                                     void *stream);
+
+/*
  * Dedup compaction of top-k lists (README, "4-bit KV cache": dedup
  * compaction).  For each list l in [0, n_lists), independently: walk
  * idx[l * idx_row_stride + 0..k-1] in order, keep the first occurrence of
@@ -137,10 +153,10 @@ kv4_status kv4_write_and_dedup(const float *kv, int64_t kv_row_stride, const int
 /*
  * Arguments of the attention entry points.  For query row r and head h the
  * result is, over the valid entries j of row r's list,
- *   s_j = sm_scale * sum_{i<576} q[r, h, i] * K_j[i]
+ *   s_j = sm_scale * sum_{i<D} q[r, h, i] * K_j[i]     (D = 576, or 512 rope-free)
  *   o[r, h, :] = sum_j exp(s_j - m) V_j / sum_j exp(s_j - m),   m = max_j s_j
  *   lse[r, h]  = m + ln sum_j exp(s_j - m)
- * where K_j is the dequantized row of entry j (576 values) and V_j its first
+ * where K_j is the dequantized row of entry j (D values) and V_j its first
  * 512 (the latent part: the absorbed-MLA attention core, W_UK applied before
  * and W_UV after it, sgl-amd-mono GLM-5.3 PR, "How a decode step runs").
  * Entry j of row r: pos = topk[r * topk_row_stride + j]; pos < 0 is skipped;
@@ -152,12 +168,12 @@ kv4_status kv4_write_and_dedup(const float *kv, int64_t kv_row_stride, const int
 typedef struct kv4_attn_args {
     uint32_t struct_size;      /* must equal sizeof(kv4_attn_args) */
     kv4_dtype q_dtype;         /* KV4_BF16 or KV4_F32 */
-    const void *q;             /* device [n_rows, n_heads, 576]; 16-byte aligned */
+    const void *q;             /* device [n_rows, n_heads, D]; 16-byte aligned */
     int64_t q_row_stride;      /* elements; multiple of 8 (bf16) or 4 (f32) */
-    int64_t q_head_stride;     /* elements; >= 576, multiple of 8 (bf16) or 4 (f32) */
+    int64_t q_head_stride;     /* elements; >= D, multiple of 8 (bf16) or 4 (f32) */
     int32_t n_rows;            /* query rows (decode: one per request) */
     int32_t n_heads;           /* multiple of 16, 16..128 */
-    const uint8_t *pool;       /* device [n_slots, 352]; 16-byte aligned */
+    const uint8_t *pool;       /* device [n_slots, 352 or 288 (rope-free)]; 16-byte aligned */
     int64_t n_slots;
     const int32_t *page_table; /* device, nullable: NULL => list entries are slots */
     int64_t pt_row_stride;     /* elements between page-table rows (0 = shared row) */
@@ -174,6 +190,7 @@ typedef struct kv4_attn_args {
     int64_t out_row_stride;    /* elements, >= n_heads * 512, multiple of 4 */
     float *lse;                /* device [n_rows, n_heads] fp32, nullable */
     uint32_t *err_word;        /* device, nullable */
+    kv4_row_format row_format; /* KV4_ROW_ROPE (0; D = 576) or KV4_ROW_ROPE_FREE (D = 512) */
 } kv4_attn_args;
 
 /* Number of splits kv4_sparse_mla_decode uses for num_splits = 0, or a
@@ -234,12 +251,13 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
 /*
  * Dequantizing gather (README, "4-bit KV cache": the dequantizing gather).
  * For query row r and list entry j < k (translated exactly as above), writes
- * the entry's 576 dequantized values as fp16 bit patterns to
- * out[(r * k + j) * 576 + i] and its pool slot to slots_out[r * k + j];
- * skipped entries get 576 zeros and slot -1.  Every value is exact in fp16
- * (an E2M1 x E4M3 product or an E4M3 value).  The attention entry points
- * never build this copy; it serves callers that want the rows themselves.
- *   out           device [n_rows, k, 576] uint16 (fp16 bits), 16-byte aligned.
+ * the entry's D dequantized values (D = 576, or 512 for rope-free rows) as
+ * fp16 bit patterns to out[(r * k + j) * D + i] and its pool slot to
+ * slots_out[r * k + j]; skipped entries get D zeros and slot -1.  Every value
+ * is exact in fp16 (an E2M1 x E4M3 product or an E4M3 value).  The attention
+ * entry points never build this copy; it serves callers that want the rows
+ * themselves.
+ *   out           device [n_rows, k, D] uint16 (fp16 bits), 16-byte aligned.
  *   slots_out     device [n_rows, k] int32, nullable.
  * a->q, a->out and a->lse are ignored.  Errors: as kv4_sparse_mla_decode.
  */
