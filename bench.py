@@ -46,6 +46,7 @@ def _args():
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-write", action="store_true", help="skip the write + compaction measurement")
+    ap.add_argument("--no-rope-free", action="store_true", help="skip the rope-free (288-byte row) decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size kernel for counter calibration)")
@@ -104,11 +105,12 @@ def gathered_rows_host(spec, pt_h, topk_h, dev):
 
 
 # ---------------------------------------------------------- measurement
-def algorithmic_decode_bytes(n_req, n_heads, k, q_bytes=2):
-    """Per launch: each request's k selected rows (352 B), k list entries and
-    k page-table entries (4 B each), its queries (n_heads x 576 x q_bytes) and
-    its output (n_heads x 512 fp32 + n_heads lse)."""
-    per_req = k * 352 + k * 4 * 2 + n_heads * 576 * q_bytes + n_heads * (512 + 1) * 4
+def algorithmic_decode_bytes(n_req, n_heads, k, q_bytes=2, row_bytes=352, dim=576):
+    """Per launch: each request's k selected rows (row_bytes: 352, or 288
+    rope-free), k list entries and k page-table entries (4 B each), its
+    queries (n_heads x dim x q_bytes) and its output (n_heads x 512 fp32 +
+    n_heads lse)."""
+    per_req = k * row_bytes + k * 4 * 2 + n_heads * dim * q_bytes + n_heads * (512 + 1) * 4
     return per_req * n_req
 
 
@@ -323,6 +325,8 @@ def main():
         "decode_gbs_incl_merge": round(algo / ((split_ms + merge_ms) * 1e-3) / 1e9, 1),
     }
 
+    if not args.no_rope_free:
+        result["rope_free_decode"] = run_rope_free(spec, wl, dev, S, launch_ms)
     if not args.no_prefill:
         del part_o
         result["prefill"] = run_prefill(args, dev)
@@ -332,6 +336,40 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = run_cpu_baseline(spec, wl, dev)
     print(json.dumps(result), flush=True)
+
+
+def run_rope_free(spec, wl, dev, S, launch_ms):
+    """The same decode over the 288-byte rope-free rows (the latent part of
+    the same device-drawn rows, 512-dim queries): the pool is built the same
+    way, the lists and page table are the workload's."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+    print("[bench] rope-free decode %s" % spec.name, file=sys.stderr, flush=True)
+    pool = torch.empty((spec.n_slots, kv4.ROW_BYTES_ROPE_FREE), dtype=torch.uint8, device=dev)
+    for c in range(-(-spec.n_slots // W.KV_CHUNK)):
+        x = W.kv_chunk_device(spec, c, dev)            # [n, 576]: the write reads the first 512 of each row
+        lo = c * W.KV_CHUNK
+        kv4.quant_write(x, torch.arange(lo, lo + x.shape[0], dtype=torch.int32, device=dev), pool)
+        del x
+    st = wl["sets"][0]
+    q = st["q"][:, :, :512].contiguous()
+    scale = 1.0 / np.sqrt(512.0)
+    R, H, K = spec.n_req, spec.n_heads, spec.k
+    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(q, pool, st["topk"], S, page_table=wl["pt"])),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    ms = launch_ms(lambda: kv4.sparse_mla_decode(q, pool, st["topk"], scale, page_table=wl["pt"], num_splits=S,
+                                                 workspace=ws, out=out, lse=lse))
+    algo = algorithmic_decode_bytes(R, H, K, row_bytes=kv4.ROW_BYTES_ROPE_FREE, dim=512)
+    del pool
+    torch.cuda.empty_cache()
+    gbs = algo / (ms * 1e-3) / 1e9
+    return {"workload": spec.name + " with 288-byte rope-free rows", "row_bytes": kv4.ROW_BYTES_ROPE_FREE,
+            "splits": S, "decode_ms": round(ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
+            "algorithmic_bytes": algo, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "one decode call (split kernel and merge) per token batch; the step's write and dedup not included"}
 
 
 def run_write_compaction(dev):
