@@ -72,6 +72,8 @@ def _load(path: str):
     L.o_dedup_compact.argtypes, L.o_dedup_compact.restype = [vp, i64, i32, i64, vp, vp], None
     L.o_translate.argtypes, L.o_translate.restype = [i32, vp, i32, i32, i64, vp], i64
     L.o_sparse_mla.argtypes, L.o_sparse_mla.restype = [ctypes.POINTER(_AttnArgs), vp, vp, vp, vp], None
+    L.o_global_compact.argtypes = [vp, i32, i32, i64, vp, i64, i32, i32, i32, vp, vp, i64, ctypes.c_int, vp, vp, vp]
+    L.o_global_compact.restype = i64
     L.o_merge_states.argtypes = [vp, vp, ctypes.c_int, i64, ctypes.c_int, vp, vp]
     L.o_merge_states.restype = None
     L.o_num_threads.argtypes, L.o_num_threads.restype = [], ctypes.c_int
@@ -189,6 +191,31 @@ def translate(pos: int, pt_row=None, page_size: int = 64, n_slots: int = 1 << 62
     s = lib().o_translate(int(pos), _ptr(pt_row), 0 if pt_row is None else pt_row.shape[0],
                           page_size, n_slots, _ptr(err))
     return int(s), int(err[0])
+
+
+# ------------------------------------------------- global dedup across lists
+def global_compact(topk, pool, page_table=None, row_req=None, page_size: int = 64):
+    """The compacted pool: (cpool [|U|, row_bytes] u8, out_idx [R, k] int32, |U|, err bits).
+    U = the distinct valid translated slots of all lists, increasing; out_idx holds
+    each entry's index in U (-1 when skipped)."""
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    pool = np.ascontiguousarray(pool, dtype=np.uint8)
+    R, k = topk.shape
+    rb = pool.shape[1]
+    if page_table is not None:
+        page_table = np.ascontiguousarray(page_table, dtype=np.int32)
+    if row_req is not None:
+        row_req = np.ascontiguousarray(row_req, dtype=np.int32)
+    cap = min(pool.shape[0], R * k)
+    cpool = np.zeros((max(cap, 1), rb), dtype=np.uint8)
+    out_idx = np.zeros((R, k), dtype=np.int32)
+    err = np.zeros(1, dtype=np.uint32)
+    n = lib().o_global_compact(_ptr(topk), R, k, k, _ptr(page_table),
+                               0 if page_table is None else page_table.shape[1],
+                               0 if page_table is None else page_table.shape[0],
+                               0 if page_table is None else page_table.shape[1], page_size, _ptr(row_req),
+                               _ptr(pool), pool.shape[0], rb, _ptr(cpool), _ptr(out_idx), _ptr(err))
+    return cpool[:n], out_idx, int(n), int(err[0])
 
 
 # --------------------------------------------------------------- attention

@@ -284,6 +284,60 @@ int64_t o_translate(int32_t pos, const int32_t *pt_row, int32_t pt_n_pages, int3
     return slot;
 }
 
+/* ------------------------------------------------ global dedup across lists */
+
+/* The compacted pool ([P1-KV4] "dedup compaction" read across all lists at
+ * once).  Every entry of every list is translated as for attention (entries
+ * of a query row whose request is outside [0, pt_n_rows) are skipped and
+ * flag ERR_PAGE when >= 0).  U = the distinct valid slots in increasing
+ * order; cpool row i = pool row U[i]; out_idx[r * k + j] = the index in U of
+ * entry (r, j)'s slot, -1 for a skipped entry.  Returns |U|.  Attention over
+ * cpool with out_idx as physical slots equals attention over pool with the
+ * original lists, entry for entry. */
+int64_t o_global_compact(const int32_t *topk, int32_t n_rows, int32_t k, int64_t topk_row_stride,
+                         const int32_t *page_table, int64_t pt_row_stride, int32_t pt_n_rows, int32_t pt_n_pages,
+                         int32_t page_size, const int32_t *row_req, const uint8_t *pool, int64_t n_slots,
+                         int row_bytes, uint8_t *cpool, int32_t *out_idx, uint32_t *err)
+{
+    char *seen = (char *)calloc((size_t)(n_slots > 0 ? n_slots : 1), 1);
+    int64_t *rank = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_slots > 0 ? n_slots : 1));
+    int64_t count = 0, s;
+    int32_t r, j;
+    int pass;
+    for (pass = 0; pass < 2; ++pass) {        /* 0: mark the slots; 1: rewrite the lists */
+        for (r = 0; r < n_rows; ++r) {
+            int32_t req = row_req ? row_req[r] : r;
+            int bad = page_table && (req < 0 || req >= pt_n_rows);
+            const int32_t *pt_row = page_table && !bad ? page_table + (int64_t)req * pt_row_stride : NULL;
+            for (j = 0; j < k; ++j) {
+                int32_t pos = topk[(int64_t)r * topk_row_stride + j];
+                int64_t slot = -1;
+                if (bad) {
+                    if (pos >= 0) *err |= ERR_PAGE;
+                } else {
+                    slot = o_translate(pos, pt_row, pt_n_pages, page_size, n_slots, err);
+                }
+                if (pass == 0) {
+                    if (slot >= 0) seen[slot] = 1;
+                } else {
+                    out_idx[(int64_t)r * k + j] = slot >= 0 ? (int32_t)rank[slot] : -1;
+                }
+            }
+        }
+        if (pass == 0) {
+            for (s = 0; s < n_slots; ++s) {
+                if (!seen[s]) continue;
+                rank[s] = count;
+                memcpy(cpool + count * row_bytes, pool + s * row_bytes, (size_t)row_bytes);
+                ++count;
+            }
+        }
+    }
+    free(seen);
+    free(rank);
+    return count;
+}
+
 /* ------------------------------------------------------ sparse MLA attention */
 
 /* One argument block shared by the attention entry points.  q is fp32

@@ -36,6 +36,9 @@ MUTATIONS = [
     ("dedup_keeps_last", "if (j == 0 || pairs[j].v != pairs[j - 1].v) keep[nk++] = pairs[j].pos;",
      "if (j == np - 1 || pairs[j].v != pairs[j + 1].v) keep[nk++] = pairs[j].pos;", ["dedup"]),
     ("merge_weight_sign", "w = exp(ls - M);", "w = exp(M - ls);", ["merge"]),
+    ("compact_rank_skips_one", "rank[s] = count;", "rank[s] = count + (count > 0);", ["compact"]),
+    ("compact_keeps_first_page_only", "if (slot >= 0) seen[slot] = 1;", "if (slot >= 0 && slot < 64) seen[slot] = 1;",
+     ["compact"]),
     ("rope_scaled_like_latent", "for (i = 0; i < n_rope; ++i) rope[i] = o_e4m3_encode(x[n_latent + i]);",
      "for (i = 0; i < n_rope; ++i) rope[i] = o_e4m3_encode(x[n_latent + i] / 6.0f);", ["roundtrip", "scale_argmin"]),
 ]
@@ -52,6 +55,7 @@ PINS = {
     "translate": P.test_translate_matches_page_arithmetic,
     "dedup": lambda: P.test_dedup_matches_brute_force(300),
     "merge": P.test_merge_of_split_lists_equals_whole_list,
+    "compact": lambda: P.test_global_compact_matches_brute_force(0),
 }
 
 

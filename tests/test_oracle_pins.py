@@ -284,6 +284,65 @@ def test_translate_matches_page_arithmetic():
     assert oracle.translate(4, None, 64, 5) == (4, 0)
 
 
+# ------------------------------------------- global dedup across lists
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_global_compact_matches_brute_force(seed):
+    """The compacted pool against sorted(set(...)) of slots computed here from
+    the page arithmetic, with negative entries, unmapped and out-of-table
+    pages, slots past the pool and a query row of a missing request."""
+    g = np.random.default_rng(40 + seed)
+    n_req, n_pages, R, k = 3, 6, 5, 40
+    n_slots = 20 * 64 - 7                                  # the last page is cut short
+    pool = g.integers(0, 256, size=(n_slots, 9)).astype(np.uint8)
+    pt = g.permutation(20)[:n_req * n_pages].reshape(n_req, n_pages).astype(np.int32)
+    pt[1, 2] = -1
+    row_req = np.array([0, 1, 2, 2, 7], np.int32)           # row 4 names no request
+    topk = g.integers(-3, n_pages * 64 + 30, size=(R, k)).astype(np.int32)
+    topk[0, :5] = topk[0, 5]                                 # repeats inside a list
+    topk[1, 0] = topk[2, 0]
+    cpool, out_idx, n, err = oracle.global_compact(topk, pool, pt, row_req)
+    want_err = 0
+    slots = np.full((R, k), -1, np.int64)
+    for r in range(R):
+        req = row_req[r]
+        for j in range(k):
+            pos = int(topk[r, j])
+            if pos < 0:
+                continue
+            if not 0 <= req < n_req:
+                want_err |= oracle.ERR_PAGE
+                continue
+            page = pos // 64
+            if page >= n_pages or pt[req, page] < 0:
+                want_err |= oracle.ERR_PAGE
+                continue
+            slot = int(pt[req, page]) * 64 + pos % 64
+            if slot >= n_slots:
+                want_err |= oracle.ERR_SLOT
+                continue
+            slots[r, j] = slot
+    uniq = sorted(set(int(x) for x in slots.ravel() if x >= 0))
+    assert n == len(uniq) and err == want_err
+    assert (cpool == pool[uniq]).all()
+    where = {s_: i for i, s_ in enumerate(uniq)}
+    want_idx = np.array([[where[int(x)] if x >= 0 else -1 for x in row] for row in slots], np.int32)
+    assert (out_idx == want_idx).all()
+
+
+def test_global_compact_keeps_attention_exactly():
+    """Attention over the compacted pool, its lists taken as physical slots,
+    equals attention over the original pool entry for entry (bitwise)."""
+    g, pool, pt, q, ctx = _tiny_case(77, n_pages=6, n_heads=2)
+    topk = np.stack([g.choice(ctx, 50, replace=False) for _ in range(1)]).astype(np.int32)
+    topk[0, 3] = -1
+    topk[0, 7] = topk[0, 8]
+    cpool, out_idx, n, err = oracle.global_compact(topk, pool, pt)
+    assert err == 0 and n == len(set(topk[0][topk[0] >= 0].tolist()))
+    a = oracle.sparse_mla(q, pool, topk, 0.05, page_table=pt)
+    b = oracle.sparse_mla(q, cpool, out_idx, 0.05)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 # ------------------------------------------------------------ attention
 def _tiny_case(seed, n_pages=4, n_heads=3, ctx=None, q_scale=1.0):
     g = np.random.default_rng(seed)
