@@ -47,6 +47,7 @@ def _args():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-write", action="store_true", help="skip the write + compaction measurement")
     ap.add_argument("--no-rope-free", action="store_true", help="skip the rope-free (288-byte row) decode measurement")
+    ap.add_argument("--no-compact", action="store_true", help="skip the global compaction measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size kernel for counter calibration)")
@@ -327,6 +328,10 @@ def main():
 
     if not args.no_rope_free:
         result["rope_free_decode"] = run_rope_free(spec, wl, dev, S, launch_ms)
+    if not args.no_compact:
+        print("[bench] global compaction of the decode lists", file=sys.stderr, flush=True)
+        result["global_compact_decode"] = run_global_compact(spec.name + " lists", pool, sets[0]["topk"], pt, None,
+                                                             dev)[0]
     if not args.no_prefill:
         del part_o
         result["prefill"] = run_prefill(args, dev)
@@ -370,6 +375,45 @@ def run_rope_free(spec, wl, dev, S, launch_ms):
             "splits": S, "decode_ms": round(ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
             "algorithmic_bytes": algo, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "note": "one decode call (split kernel and merge) per token batch; the step's write and dedup not included"}
+
+
+def run_global_compact(name, pool, topk, pt, row_req, dev, reps=5):
+    """Global dedup across all lists into a compacted pool: average time of a
+    HIP graph of `reps` calls (six kernels each); algorithmic bytes = lists
+    read and rewritten, page-table entries, the slot bitmap written and read
+    twice, and the distinct rows read and written."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    R, k = topk.shape
+    cap = min(pool.shape[0], R * k)
+    cpool = torch.empty((max(cap, 1), pool.shape[1]), dtype=torch.uint8, device=dev)
+    out_idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, kv4.global_compact_workspace(pool, topk, page_table=pt, row_req=row_req)),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(page_table=pt, row_req=row_req, cpool=cpool, out_idx=out_idx, out_count=cnt, workspace=ws)
+    kv4.global_compact(pool, topk, **kw)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            kv4.global_compact(pool, topk, **kw)
+    g.replay()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) / (3 * reps) * 1e3
+    n = int(cnt.item())
+    bitmap = (pool.shape[0] + 7) // 8
+    algo = R * k * 4 * 3 + bitmap * 3 + n * pool.shape[1] * 2
+    return {"lists": name, "entries": R * k, "distinct_rows": n, "row_bytes": pool.shape[1], "us": round(us, 2),
+            "algorithmic_bytes": algo, "gbs": round(algo / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}, cpool[:n], out_idx
 
 
 def run_write_compaction(dev):
@@ -454,10 +498,26 @@ def run_prefill(args, dev):
     t = float(np.median(ms))
     fl = prefill_flops(spec.rows, spec.n_heads, spec.k)
     tf = fl / (t * 1e-3) / 1e12
-    return {"workload": spec.name, "query_rows": spec.rows, "heads": spec.n_heads, "topk": spec.k,
-            "context_tokens": spec.ctx, "ms": round(t, 4), "tflops": round(tf, 2),
-            "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-            "query_tokens_per_s": round(spec.rows / (t * 1e-3), 1)}
+    res = {"workload": spec.name, "query_rows": spec.rows, "heads": spec.n_heads, "topk": spec.k,
+           "context_tokens": spec.ctx, "ms": round(t, 4), "tflops": round(tf, 2),
+           "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS, "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+           "query_tokens_per_s": round(spec.rows / (t * 1e-3), 1)}
+    if not args.no_compact:
+        # the prefill lists compacted into one pool, then the prefill over it
+        comp, cpool, cidx = run_global_compact(spec.name + " lists", pool, topk, pt, rr, dev)
+        kv4.sparse_mla_prefill(q, cpool, cidx, spec.sm_scale, out=out, lse=lse)
+        torch.cuda.synchronize(dev)
+        cms = []
+        for _ in range(args.prefill_iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kv4.sparse_mla_prefill(q, cpool, cidx, spec.sm_scale, out=out, lse=lse)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            cms.append(e0.elapsed_time(e1))
+        comp["prefill_over_compacted_pool_ms"] = round(float(np.median(cms)), 4)
+        res["global_compact"] = comp
+    return res
 
 
 if __name__ == "__main__":

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "Kv4Error", "ROW_BYTES", "ROW_BYTES_ROPE_FREE", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
     "library_path", "load", "version", "last_error",
-    "quant_write", "dedup_compact", "write_and_dedup", "sparse_mla_decode", "sparse_mla_decode_partial",
+    "quant_write", "dedup_compact", "write_and_dedup", "global_compact", "global_compact_workspace", "sparse_mla_decode", "sparse_mla_decode_partial",
     "sparse_mla_decode_splits", "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill",
     "gather_dequant",
 ]
@@ -89,6 +89,8 @@ def load():
     L.kv4_quant_write_rope_free.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
     L.kv4_dedup_compact.argtypes = [vp, i64, i32, i64, vp, vp, vp]
     L.kv4_write_and_dedup.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i32, i64, vp, vp, vp]
+    L.kv4_global_compact_workspace.argtypes, L.kv4_global_compact_workspace.restype = [pa], sz
+    L.kv4_global_compact.argtypes = [pa, vp, i64, vp, vp, vp, sz, vp]
     L.kv4_sparse_mla_decode_splits.argtypes, L.kv4_sparse_mla_decode_splits.restype = [pa], i32
     L.kv4_sparse_mla_decode_workspace.argtypes, L.kv4_sparse_mla_decode_workspace.restype = [pa, i32], sz
     L.kv4_sparse_mla_decode.argtypes = [pa, i32, vp, sz, vp]
@@ -225,7 +227,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
     if q.dim() != 3 or q.shape[2] != dim or q.stride(2) != 1:
         raise ValueError("q must be [n_rows, n_heads, %d] with unit inner stride for a %d-byte pool"
                          % (dim, pool.shape[1]))
-    if topk.dim() != 2 or topk.stride(1) != 1 or topk.shape[0] != q.shape[0]:
+    if topk.dim() != 2 or topk.shape[0] != q.shape[0] or (topk.numel() > 0 and topk.stride(1) != 1):
         raise ValueError("topk must be [n_rows, k] with unit inner stride")
     a = AttnArgs()
     a.struct_size = ctypes.sizeof(AttnArgs)
@@ -351,6 +353,51 @@ def sparse_mla_prefill(q, pool, topk, sm_scale, page_table=None, row_req=None, p
     a = _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse, err_word)
     _check(load().kv4_sparse_mla_prefill(ctypes.byref(a), _stream(stream, q.device)))
     return out, lse
+
+
+def _compact_args(pool, topk, page_table, row_req, page_size, err_word):
+    R = topk.shape[0]
+    rope_free = pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE
+    dummy_q = torch.empty((R, 16, LATENT if rope_free else DIM), dtype=torch.bfloat16, device=topk.device)
+    return _attn_args(dummy_q, pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
+
+
+def global_compact_workspace(pool, topk, page_table=None, row_req=None, page_size=64) -> int:
+    """kv4_global_compact_workspace: bytes of the compaction's workspace for these arguments."""
+    a = _compact_args(pool, topk, page_table, row_req, page_size, None)
+    return int(load().kv4_global_compact_workspace(ctypes.byref(a)))
+
+
+def global_compact(pool, topk, page_table=None, row_req=None, page_size=64, err_word=None, cpool=None, out_idx=None,
+                   out_count=None, workspace=None, stream=None):
+    """kv4_global_compact: the distinct valid slots U of all lists, in increasing order; returns
+    (cpool [min(n_slots, R*k), row bytes] with rows U in its first |U| rows, out_idx [R, k] int32
+    with each entry's index in U or -1, out_count [1] int32 = |U|) (device tensors; nothing is
+    synchronized)."""
+    R, k = topk.shape[0], topk.shape[1]
+    a = _compact_args(pool, topk, page_table, row_req, page_size, err_word)
+    L = load()
+    cap = min(pool.shape[0], R * k)
+    if cpool is None:
+        cpool = torch.empty((max(cap, 1), pool.shape[1]), dtype=torch.uint8, device=pool.device)
+    if out_idx is None:
+        out_idx = torch.empty((R, k), dtype=torch.int32, device=pool.device)
+    if out_count is None:
+        out_count = torch.empty((1,), dtype=torch.int32, device=pool.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, int(L.kv4_global_compact_workspace(ctypes.byref(a)))), dtype=torch.uint8,
+                                device=pool.device)
+    _need(cpool, "cpool", torch.uint8, pool.device)
+    _need(out_idx, "out_idx", torch.int32, pool.device)
+    _need(out_count, "out_count", torch.int32, pool.device)
+    _need(workspace, "workspace", torch.uint8, pool.device)
+    if not cpool.is_contiguous() or cpool.dim() != 2 or cpool.shape[1] != pool.shape[1]:
+        raise ValueError("cpool must be contiguous [rows, %d]" % pool.shape[1])
+    if not out_idx.is_contiguous() or tuple(out_idx.shape) != (R, k):
+        raise ValueError("out_idx must be contiguous [n_rows, k]")
+    _check(L.kv4_global_compact(ctypes.byref(a), _ptr(cpool), cpool.shape[0], _ptr(out_idx), _ptr(out_count),
+                                _ptr(workspace), workspace.numel(), _stream(stream, pool.device)))
+    return cpool, out_idx, out_count
 
 
 def gather_dequant(pool, topk, page_table=None, row_req=None, page_size=64, err_word=None, stream=None):

@@ -368,6 +368,50 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
     return hip_status(kv4::launch_merge_states(m, (hipStream_t)stream), "merge_states launch");
 }
 
+size_t kv4_global_compact_workspace(const kv4_attn_args *a) {
+    if (check_attn(a, false) != KV4_OK) return 0;
+    return kv4::compact_workspace(a->pool ? a->n_slots : 0, (int64_t)a->n_rows * a->k).bytes;
+}
+
+kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cpool_rows, int32_t *out_idx,
+                              int32_t *out_count, void *workspace, size_t workspace_bytes, void *stream) {
+    const kv4_status st = check_attn(a, false);
+    if (st != KV4_OK) return st;
+    if (!out_count) return fail(KV4_ERR_NULL, "out_count is NULL");
+    const int64_t n_slots = a->pool ? a->n_slots : 0;
+    if (n_slots > 0x7FFFFFFF) return fail(KV4_ERR_UNSUPPORTED, "n_slots = %lld; at most 2^31 - 1", (long long)n_slots);
+    const int64_t n_entries = (int64_t)a->n_rows * a->k;
+    const kv4::CompactWorkspace w = kv4::compact_workspace(n_slots, n_entries);
+    if (n_entries > 0 && !out_idx) return fail(KV4_ERR_NULL, "out_idx is NULL");
+    if (cpool_rows < w.max_rows)
+        return fail(KV4_ERR_SHAPE, "cpool has %lld rows; min(n_slots, n_rows * k) = %lld needed", (long long)cpool_rows,
+                    (long long)w.max_rows);
+    if (w.max_rows > 0 && !cpool) return fail(KV4_ERR_NULL, "cpool is NULL");
+    if (cpool && !aligned(cpool, 16)) return fail(KV4_ERR_ALIGN, "cpool must be 16-byte aligned");
+    if (!workspace || workspace_bytes < w.bytes)
+        return fail(KV4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, w.bytes);
+    if (!aligned(workspace, 256)) return fail(KV4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    kv4::CompactParams p{};
+    p.topk = a->topk;
+    p.topk_row_stride = a->topk_row_stride;
+    p.n_rows = a->n_rows;
+    p.k = a->k;
+    p.page_table = a->page_table;
+    p.pt_row_stride = a->pt_row_stride;
+    p.pt_n_rows = a->pt_n_rows;
+    p.pt_n_pages = a->pt_n_pages;
+    p.page_shift = page_shift(a);
+    p.row_req = a->row_req;
+    p.pool = a->pool;
+    p.n_slots = n_slots;
+    p.row_bytes = a->row_format == KV4_ROW_ROPE_FREE ? KV4_ROW_BYTES_ROPE_FREE : KV4_ROW_BYTES;
+    p.cpool = cpool;
+    p.out_idx = out_idx;
+    p.out_count = out_count;
+    p.err_word = a->err_word;
+    return hip_status(kv4::launch_global_compact(p, workspace, (hipStream_t)stream), "global_compact launch");
+}
+
 kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *slots_out, void *stream) {
     const kv4_status st = check_attn(a, false);
     if (st != KV4_OK) return st;

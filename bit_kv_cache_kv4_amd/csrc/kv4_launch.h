@@ -69,6 +69,33 @@ hipError_t launch_sparse_mla(const AttnParams &p, bool q_f32, int32_t n_splits, 
 // grid = (n_rows, ceil(k / 32)); out[(r * k + j) * 576 + i] fp16 bits, slots_out nullable
 hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *slots_out, hipStream_t stream);
 
+// Global dedup across lists into a compacted pool (kv4_compact.hip).
+struct CompactParams {
+    const int32_t *topk;
+    int64_t topk_row_stride;
+    int32_t n_rows, k;
+    const int32_t *page_table;
+    int64_t pt_row_stride;
+    int32_t pt_n_rows, pt_n_pages, page_shift;
+    const int32_t *row_req;
+    const uint8_t *pool;
+    int64_t n_slots;
+    int32_t row_bytes;         // 352 or 288
+    uint8_t *cpool;            // [max_rows, row_bytes]
+    int32_t *out_idx;          // [n_rows, k]
+    int32_t *out_count;        // [1]: |U|
+    uint32_t *err_word;
+};
+
+// Workspace layout of the compaction: slot bitmap, per-word and per-block
+// prefixes, and the list U of slots (each part 256-byte aligned).
+struct CompactWorkspace {
+    int64_t n_words, n_blocks, max_rows;
+    size_t bitmap_off, word_base_off, block_sum_off, block_base_off, uslots_off, bytes;
+};
+CompactWorkspace compact_workspace(int64_t n_slots, int64_t n_entries);
+hipError_t launch_global_compact(const CompactParams &p, void *workspace, hipStream_t stream);
+
 struct MergeParams {
     const float *part_o;       // (s, t, d) at (s * n_states + t) * dim + d
     const float *part_lse;     // (s, t) at s * n_states + t

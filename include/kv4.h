@@ -264,6 +264,31 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
 kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *slots_out, void *stream);
 
 /*
+ * Global dedup across lists into a compacted pool (README, "4-bit KV cache":
+ * dedup compaction, here across all lists at once).  Every entry of every
+ * list is translated exactly as the attention entry points translate it (a
+ * query row whose request is outside the page table skips its entries and
+ * sets KV4_ERRBIT_PAGE).  With U the distinct valid slots in increasing
+ * order: cpool row i = pool row U[i] (i < |U|), out_idx[r * k + j] = the
+ * index in U of entry (r, j)'s slot or -1, *out_count = |U|.  Attention with
+ * pool = cpool, page_table = NULL and topk = out_idx equals attention over
+ * the original arguments, entry for entry; the rows it gathers are |U|
+ * contiguous ones.
+ *   a             the attention arguments (q must pass the argument checks
+ *                 but is not read; out and lse are ignored).
+ *   cpool         device [cpool_rows, row bytes of a->row_format], 16-byte
+ *                 aligned; cpool_rows >= min(n_slots, n_rows * k).
+ *   out_idx       device int32 [n_rows, k]; out_count device int32 [1].
+ *   workspace     device, >= kv4_global_compact_workspace(a) bytes, 256-byte
+ *                 aligned (a bitmap of n_slots bits, prefixes and U).
+ * Errors: those of kv4_sparse_mla_decode, KV4_ERR_WORKSPACE, and
+ * KV4_ERR_UNSUPPORTED for n_slots >= 2^31.
+ */
+size_t kv4_global_compact_workspace(const kv4_attn_args *a);
+kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cpool_rows, int32_t *out_idx,
+                              int32_t *out_count, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Sparse MLA prefill (README, "AMD MI355X": sparse MLA prefill for gfx950).
  * The same result as kv4_sparse_mla_decode for every query row, computed
  * without splitting the list: one workgroup per (query row, 64 heads) walks

@@ -164,6 +164,27 @@ def test_write_and_dedup_argument_checks():
     assert f(*w_ok, V(0x1000), 4, 16, 16, None, V(0x300000), None) == 1
 
 
+def test_global_compact_argument_checks():
+    """Workspace and output sizing of the compaction (no launch)."""
+    lib = kv4.load()
+    a = _args()                                          # 2 rows x 16 entries over 100 slots
+    need = lib.kv4_global_compact_workspace(ctypes.byref(a))
+    assert need > 0
+    V = ctypes.c_void_p
+    f = lib.kv4_global_compact
+    assert f(ctypes.byref(a), V(0x10000), 32, V(0x20000), V(0x30000), V(0x100000), need - 1, None) == 5
+    assert f(ctypes.byref(a), V(0x10000), 31, V(0x20000), V(0x30000), V(0x100000), need, None) == 2   # cpool rows
+    assert "cpool" in kv4.last_error()
+    assert f(ctypes.byref(a), V(0x10000), 32, None, V(0x30000), V(0x100000), need, None) == 1           # out_idx
+    assert f(ctypes.byref(a), V(0x10000), 32, V(0x20000), None, V(0x100000), need, None) == 1           # out_count
+    assert f(ctypes.byref(a), V(0x10008), 32, V(0x20000), V(0x30000), V(0x100000), need, None) == 3     # cpool align
+    assert f(ctypes.byref(a), V(0x10000), 32, V(0x20000), V(0x30000), V(0x100010), need, None) == 3     # workspace align
+    a2 = _args(row_format=1, q_head_stride=576)                  # rope-free: 512-dim queries suffice
+    assert lib.kv4_global_compact_workspace(ctypes.byref(a2)) == need
+    a3 = _args(row_format=2)
+    assert lib.kv4_global_compact_workspace(ctypes.byref(a3)) == 0
+
+
 def test_merge_argument_checks():
     lib = kv4.load()
     f = lib.kv4_merge_states
