@@ -379,9 +379,10 @@ def run_rope_free(spec, wl, dev, S, launch_ms):
 
 def run_global_compact(name, pool, topk, pt, row_req, dev, reps=5):
     """Global dedup across all lists into a compacted pool: average time of a
-    HIP graph of `reps` calls (six kernels each); algorithmic bytes = lists
-    read and rewritten, page-table entries, the slot bitmap written and read
-    twice, and the distinct rows read and written."""
+    HIP graph of `reps` calls (six kernels each); algorithmic bytes = the
+    lists read twice (marking, rewriting) and the rewritten lists written, the
+    slot bitmap written and read twice, and the distinct rows read and
+    written (page-table entries are not counted: they stay in L2)."""
     import torch
     import bit_kv_cache_kv4_amd as kv4
     R, k = topk.shape
