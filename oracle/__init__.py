@@ -69,6 +69,9 @@ def _load(path: str):
     L.o_dequantize_row.argtypes, L.o_dequantize_row.restype = [vp, ctypes.c_int, ctypes.c_int, vp], None
     L.o_quant_write.argtypes = [vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp, i64, vp]
     L.o_quant_write.restype = None
+    L.o_quantize_row_mse.argtypes, L.o_quantize_row_mse.restype = [vp, ctypes.c_int, ctypes.c_int, vp], None
+    L.o_quant_write_mse.argtypes = [vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    L.o_quant_write_mse.restype = None
     L.o_dedup_compact.argtypes, L.o_dedup_compact.restype = [vp, i64, i32, i64, vp, vp], None
     L.o_translate.argtypes, L.o_translate.restype = [i32, vp, i32, i32, i64, vp], i64
     L.o_sparse_mla.argtypes, L.o_sparse_mla.restype = [ctypes.POINTER(_AttnArgs), vp, vp, vp, vp], None
@@ -135,11 +138,12 @@ def row_bytes(n_latent: int = 512, n_rope: int = 64) -> int:
     return lib().o_row_bytes(n_latent, n_rope)
 
 
-def quantize_row(x, n_latent: int = 512, n_rope: int = 64) -> np.ndarray:
+def quantize_row(x, n_latent: int = 512, n_rope: int = 64, mse: bool = False) -> np.ndarray:
+    """One row's bytes; mse=True takes the MSE-searched block scales."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     assert x.shape == (n_latent + n_rope,)
     out = np.zeros(row_bytes(n_latent, n_rope), dtype=np.uint8)
-    lib().o_quantize_row(_ptr(x), n_latent, n_rope, _ptr(out))
+    (lib().o_quantize_row_mse if mse else lib().o_quantize_row)(_ptr(x), n_latent, n_rope, _ptr(out))
     return out
 
 
@@ -158,8 +162,9 @@ def dequantize_rows(rows, n_latent: int = 512, n_rope: int = 64) -> np.ndarray:
 
 
 # ----------------------------------------------------------- quantized write
-def quant_write(kv, slots, pool, n_latent: int = 512, n_rope: int = 64) -> int:
-    """Quantize kv[n] into pool[slots[n]] in place; returns the error bits."""
+def quant_write(kv, slots, pool, n_latent: int = 512, n_rope: int = 64, mse: bool = False) -> int:
+    """Quantize kv[n] into pool[slots[n]] in place; returns the error bits.
+    mse=True takes the MSE-searched block scales."""
     kv = np.ascontiguousarray(kv, dtype=np.float32)
     slots = np.ascontiguousarray(slots, dtype=np.int32)
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
@@ -167,8 +172,8 @@ def quant_write(kv, slots, pool, n_latent: int = 512, n_rope: int = 64) -> int:
     assert pool.ndim == 2 and pool.shape[1] == rb
     assert kv.ndim == 2 and kv.shape[1] == n_latent + n_rope and kv.shape[0] == slots.shape[0]
     err = np.zeros(1, dtype=np.uint32)
-    lib().o_quant_write(_ptr(kv), kv.shape[1], _ptr(slots), kv.shape[0], n_latent, n_rope,
-                        _ptr(pool), pool.shape[0], _ptr(err))
+    (lib().o_quant_write_mse if mse else lib().o_quant_write)(_ptr(kv), kv.shape[1], _ptr(slots), kv.shape[0],
+                                                              n_latent, n_rope, _ptr(pool), pool.shape[0], _ptr(err))
     return int(err[0])
 
 

@@ -41,6 +41,10 @@
  *     the sum of exp(scaled score).
  *  R11 dedup keeps, per list, the first occurrence of each non-negative value
  *     in list order, then fills with -1, and reports the count.
+ *  R20 MSE-searched scale: the candidates are all finite non-negative E4M3
+ *     scales; a block's squared error is summed in fp32 in index order with
+ *     fused multiply-adds; the amax/6 scale stays unless another is strictly
+ *     better, and ties among better ones go to the smallest code.
  *
  * Precision: every decision that turns a float into a code (amax / 6, x / d)
  * is made in fp32, the precision of the kernels; attention arithmetic is fp64.
@@ -148,8 +152,48 @@ int o_row_bytes(int n_latent, int n_rope)
     return n_latent / 2 + n_latent / 16 + n_rope;
 }
 
-/* Quantize one row x[n_latent + n_rope] into out[o_row_bytes(...)]. */
-void o_quantize_row(const float *x, int n_latent, int n_rope, uint8_t *out)
+/* ---------------------------------------------------- MSE-searched scale */
+
+/* Squared error of coding the 16 values blk[0..15] with E4M3 scale `code`
+ * (R20): each value takes its R5 code (none when the scale is zero), the
+ * error x - c*d is formed in fp32 (c*d is exact there) and the squares are
+ * summed in index order, one fp32 fused multiply-add per value. */
+static float o_block_sq_error(const float *blk, uint8_t code)
+{
+    double d = o_e4m3_value(code);
+    float s = 0.0f;
+    int i;
+    for (i = 0; i < 16; ++i) {
+        float cd = 0.0f, e;
+        if (d != 0.0) cd = (float)(o_e2m1_value(o_e2m1_encode(blk[i] / (float)d)) * d);
+        e = blk[i] - cd;
+        s = fmaf(e, e, s);
+    }
+    return s;
+}
+
+/* MSE-searched block scale ([P1-KV4] DeepSeek V4 Pro pools; R20): every
+ * finite non-negative E4M3 code is a candidate.  The amax/6 scale `base`
+ * stays unless some candidate has a strictly smaller squared error; then the
+ * smallest code among those with the least error wins.  A block whose error
+ * is NaN (a NaN value) keeps `base`. */
+static uint8_t o_mse_scale(const float *blk, uint8_t base)
+{
+    uint8_t best = base;
+    float best_err = o_block_sq_error(blk, base);
+    int code;
+    for (code = 0; code <= 0x7E; ++code) {
+        float err = o_block_sq_error(blk, (uint8_t)code);
+        if (err < best_err) {
+            best_err = err;
+            best = (uint8_t)code;
+        }
+    }
+    return best;
+}
+
+/* Quantize one row with the amax/6 scale (mse = 0) or the MSE-searched one. */
+static void o_quantize_row_rule(const float *x, int n_latent, int n_rope, int mse, uint8_t *out)
 {
     int nblk = n_latent / 16, b, i;
     uint8_t *codes = out, *scales = out + n_latent / 2, *rope = scales + nblk;
@@ -164,6 +208,7 @@ void o_quantize_row(const float *x, int n_latent, int n_rope, uint8_t *out)
         }
         scale_f = amax / 6.0f;                 /* fp32 division (R4) */
         s = o_e4m3_encode(scale_f);
+        if (mse) s = o_mse_scale(x + 16 * b, s);
         d = o_e4m3_value(s);
         scales[b] = s;
         if (d == 0.0) continue;                /* zero block: codes stay 0 */
@@ -176,6 +221,18 @@ void o_quantize_row(const float *x, int n_latent, int n_rope, uint8_t *out)
         }
     }
     for (i = 0; i < n_rope; ++i) rope[i] = o_e4m3_encode(x[n_latent + i]);
+}
+
+/* Quantize one row x[n_latent + n_rope] into out[o_row_bytes(...)]. */
+void o_quantize_row(const float *x, int n_latent, int n_rope, uint8_t *out)
+{
+    o_quantize_row_rule(x, n_latent, n_rope, 0, out);
+}
+
+/* The same with MSE-searched block scales; rope bytes are unchanged. */
+void o_quantize_row_mse(const float *x, int n_latent, int n_rope, uint8_t *out)
+{
+    o_quantize_row_rule(x, n_latent, n_rope, 1, out);
 }
 
 /* Dequantize one row: latent value = E2M1 value * its block's E4M3 scale,
@@ -196,8 +253,8 @@ void o_dequantize_row(const uint8_t *row, int n_latent, int n_rope, double *out)
 /* For each token n with slot[n] >= 0, quantize kv[n] and store the row at
  * pool[slot * row_bytes].  A negative slot is a pad row and writes nothing
  * ([P4-PAD]); a slot >= n_slots writes nothing and sets ERR_SLOT. */
-void o_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
-                   int n_latent, int n_rope, uint8_t *pool, int64_t n_slots, uint32_t *err)
+static void o_quant_write_rule(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                               int n_latent, int n_rope, int mse, uint8_t *pool, int64_t n_slots, uint32_t *err)
 {
     int rb = o_row_bytes(n_latent, n_rope);
     uint32_t e = 0;
@@ -209,9 +266,22 @@ void o_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots,
         int32_t s = slots[n];
         if (s < 0) continue;
         if ((int64_t)s >= n_slots) { e |= ERR_SLOT; continue; }
-        o_quantize_row(kv + n * kv_row_stride, n_latent, n_rope, pool + (int64_t)s * rb);
+        o_quantize_row_rule(kv + n * kv_row_stride, n_latent, n_rope, mse, pool + (int64_t)s * rb);
     }
     if (err) *err |= e;
+}
+
+void o_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                   int n_latent, int n_rope, uint8_t *pool, int64_t n_slots, uint32_t *err)
+{
+    o_quant_write_rule(kv, kv_row_stride, slots, n_tokens, n_latent, n_rope, 0, pool, n_slots, err);
+}
+
+/* The quantized write with MSE-searched block scales (R20). */
+void o_quant_write_mse(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                       int n_latent, int n_rope, uint8_t *pool, int64_t n_slots, uint32_t *err)
+{
+    o_quant_write_rule(kv, kv_row_stride, slots, n_tokens, n_latent, n_rope, 1, pool, n_slots, err);
 }
 
 /* ------------------------------------------------------ dedup / compaction */

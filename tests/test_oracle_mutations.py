@@ -39,6 +39,12 @@ MUTATIONS = [
     ("compact_rank_skips_one", "rank[s] = count;", "rank[s] = count + (count > 0);", ["compact"]),
     ("compact_keeps_first_page_only", "if (slot >= 0) seen[slot] = 1;", "if (slot >= 0 && slot < 64) seen[slot] = 1;",
      ["compact"]),
+    ("mse_ties_to_largest_code", "if (err < best_err) {", "if (err <= best_err) {", ["mse_hand"]),
+    ("mse_search_starts_at_base", "for (code = 0; code <= 0x7E; ++code) {\n        float err",
+     "for (code = base; code <= 0x7E; ++code) {\n        float err", ["mse_brute"]),
+    ("mse_error_skips_last_value", "for (i = 0; i < 16; ++i) {\n        float cd",
+     "for (i = 0; i < 15; ++i) {\n        float cd", ["mse_brute", "mse_exact"]),
+    ("mse_absolute_error", "s = fmaf(e, e, s);", "s = s + fabsf(e);", ["mse_brute"]),
     ("rope_scaled_like_latent", "for (i = 0; i < n_rope; ++i) rope[i] = o_e4m3_encode(x[n_latent + i]);",
      "for (i = 0; i < n_rope; ++i) rope[i] = o_e4m3_encode(x[n_latent + i] / 6.0f);", ["roundtrip", "scale_argmin"]),
 ]
@@ -56,6 +62,9 @@ PINS = {
     "dedup": lambda: P.test_dedup_matches_brute_force(300),
     "merge": P.test_merge_of_split_lists_equals_whole_list,
     "compact": lambda: P.test_global_compact_matches_brute_force(0),
+    "mse_hand": P.test_mse_scale_hand_worked_block,
+    "mse_exact": P.test_mse_exact_fit_blocks_round_trip,
+    "mse_brute": lambda: [P.test_mse_scale_minimizes_squared_error_brute_force(k) for k in ("normal", "outlier")],
 }
 
 

@@ -512,3 +512,143 @@ def test_scale_uses_fp32_division_at_e4m3_midpoints():
         x[7] = a / 3
         row = oracle.quantize_row(x)
         assert row[256] == w
+
+
+# ------------------------------------------------- MSE-searched block scale
+def _e2m1_round_vec(y):
+    """Vectorized form of the independent round-half-even E2M1 grid above:
+    the E2M1 value (signed) nearest to y."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 6.0)
+    v = np.where(a < 2.0, np.rint(a * 2.0) / 2.0, np.where(a < 4.0, np.rint(a), np.rint(a / 2.0) * 2.0))
+    return np.copysign(v, y)
+
+
+def _block_errors_all_scales(blocks):
+    """fp64 squared error of every block under every finite non-negative E4M3
+    scale (codes 0..126), each value coded at the fp32 quotient x/d as R5
+    reads it; scale 0 codes every value as zero.  Independent codecs: torch's
+    E4M3 table and the rint grid."""
+    d = _torch_e4m3_decode(list(range(0x7F)))                       # [127]
+    x = blocks.astype(np.float32)[:, None, :]                        # [N, 1, 16]
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = x / d.astype(np.float32)[None, :, None]                  # fp32 quotient
+    v = _e2m1_round_vec(q) * d[None, :, None]
+    v[:, 0, :] = 0.0
+    return ((x.astype(np.float64) - v) ** 2).sum(axis=2), d          # [N, 127]
+
+
+def _row_scales_and_values(row):
+    vals = oracle.dequantize_row(row)[:512].reshape(32, 16)
+    return row[256:288].astype(int), vals
+
+
+def test_mse_scale_hand_worked_block():
+    """Block [1, 0, ..., 0]: the amax/6 scale is E4M3(1/6) = 0.171875 (0x23),
+    which codes 1 as 6 and leaves error (1 - 1.03125)^2.  The scales 0.25,
+    0.5, 1 and 2 all reproduce the block exactly; the smallest, 0.25 = 0x28,
+    wins, and the value's code is 4.0 = 0x6."""
+    x = np.zeros(576, dtype=np.float32)
+    x[0] = 1.0
+    base = oracle.quantize_row(x)
+    assert base[256] == 0x23 and (base[0] & 15) == 0x7
+    row = oracle.quantize_row(x, mse=True)
+    assert row[256] == 0x28 and (row[0] & 15) == 0x6
+    assert (row[257:288] == 0).all() and (row[1:256] == 0).all() and (row[0] >> 4) == 0
+
+
+def test_mse_exact_fit_blocks_round_trip():
+    """Blocks of E2M1 values times an E4M3 scale whose largest code need not
+    be 6: the MSE scale reproduces every block exactly, where amax/6 does not
+    for many of them (the control)."""
+    g = np.random.default_rng(21)
+    missed_by_base = 0
+    for _ in range(40):
+        x = np.zeros(576, dtype=np.float32)
+        for b in range(32):
+            d = oracle.e4m3_value(int(g.integers(8, 0x70)))
+            top = int(g.choice([3, 4, 5, 6, 7]))                     # largest magnitude code 1.5 .. 6
+            codes = g.integers(0, top + 1, size=16) | (g.integers(0, 2, size=16) << 3)
+            codes[g.integers(0, 16)] = top
+            x[16 * b:16 * b + 16] = [oracle.e2m1_value(int(c)) * d for c in codes]
+        x[512:] = g.standard_normal(64).astype(np.float32)
+        row = oracle.quantize_row(x, mse=True)
+        assert (oracle.dequantize_row(row)[:512] == x[:512]).all()
+        missed_by_base += int((oracle.dequantize_row(oracle.quantize_row(x))[:512] != x[:512]).any())
+        assert (row[288:] == oracle.quantize_row(x)[288:]).all()      # rope bytes as the plain write
+    assert missed_by_base > 20
+
+
+@pytest.mark.parametrize("kind", ["normal", "decades", "heavy", "outlier", "sparse", "tiny", "huge"])
+def test_mse_scale_minimizes_squared_error_brute_force(kind):
+    """Every block's MSE scale attains the least fp64 squared error over all
+    127 E4M3 scales (to fp32 summation accuracy), never does worse than the
+    amax/6 scale, and its codes are R5's codes at that scale."""
+    g = np.random.default_rng({"normal": 1, "decades": 2, "heavy": 3, "outlier": 4, "sparse": 5,
+                               "tiny": 6, "huge": 7}[kind])
+    n = 24
+    X = g.standard_normal((n, 576))
+    if kind == "decades":
+        X *= np.power(10.0, g.uniform(-3, 3, (n, 1)))
+    elif kind == "heavy":
+        X = g.standard_cauchy((n, 576))
+    elif kind == "outlier":
+        X[g.random((n, 576)) < 0.02] *= 40.0
+    elif kind == "sparse":
+        X[g.random((n, 576)) < 0.8] = 0.0
+    elif kind == "tiny":
+        X *= 1e-3                                # scales near and in the E4M3 subnormal range
+    elif kind == "huge":
+        X *= 600.0                               # amax/6 near the largest scale, 448
+    X = X.astype(np.float32)
+    improved = 0
+    for x in X:
+        row, base = oracle.quantize_row(x, mse=True), oracle.quantize_row(x)
+        s, _ = _row_scales_and_values(row)
+        s0, _ = _row_scales_and_values(base)
+        blocks = x[:512].reshape(32, 16)
+        err, d = _block_errors_all_scales(blocks)
+        best = err.min(axis=1)
+        got = err[np.arange(32), s]
+        e0 = err[np.arange(32), s0]
+        assert (got <= best * (1 + 1e-5)).all(), (kind, np.nonzero(got > best * (1 + 1e-5))[0])
+        assert (got <= e0 * (1 + 1e-5)).all()
+        improved += int((best < e0 * (1 - 1e-4)).sum())
+        # the codes are the nearest E2M1 values of the fp32 quotient at the chosen scale
+        vals = oracle.dequantize_row(row)[:512].reshape(32, 16)
+        dd = d[s]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = blocks / dd.astype(np.float32)[:, None]
+        want = np.where(dd[:, None] == 0.0, 0.0, _e2m1_round_vec(q) * dd[:, None])
+        assert (vals == want).all()
+        assert (row[288:] == base[288:]).all()
+    if kind not in ("sparse",):
+        assert improved > 0
+
+
+def test_mse_keeps_amax_scale_for_nan_inf_and_zero_blocks():
+    """A NaN value makes every error NaN and an infinite one every error
+    infinite, so no scale is strictly better: those blocks, and all-zero
+    blocks, keep the plain write's bytes."""
+    g = np.random.default_rng(8)
+    x = g.standard_normal(576).astype(np.float32)
+    x[3] = np.nan
+    x[40] = np.inf
+    x[77] = -np.inf
+    x[96:112] = 0.0
+    row, base = oracle.quantize_row(x, mse=True), oracle.quantize_row(x)
+    for b in (0, 2, 4, 6):
+        assert row[256 + b] == base[256 + b]
+        assert (row[8 * b:8 * b + 8] == base[8 * b:8 * b + 8]).all()
+    assert row[256 + 6] == 0 and (row[48:56] == 0).all()
+
+
+def test_mse_write_pads_and_flags():
+    g = np.random.default_rng(9)
+    kv = g.standard_normal((5, 576)).astype(np.float32)
+    pool = np.full((8, 352), 0xA5, dtype=np.uint8)
+    err = oracle.quant_write(kv, np.int32([3, -1, 8, 0, -7]), pool, mse=True)
+    assert err == oracle.ERR_SLOT
+    assert (pool[3] == oracle.quantize_row(kv[0], mse=True)).all()
+    assert (pool[0] == oracle.quantize_row(kv[3], mse=True)).all()
+    assert (pool[[1, 2, 4, 5, 6, 7]] == 0xA5).all()
