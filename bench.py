@@ -419,7 +419,8 @@ def run_global_compact(name, pool, topk, pt, row_req, dev, reps=5):
 
 def run_write_compaction(dev):
     """Config C4: quantized write of 16,384 fp32 rows into whole free pages of a
-    1024-page pool, and dedup of 4096 lists of 2048 (~25% repeats).  Eight
+    1024-page pool (amax/6 scales, and MSE-searched scales), and dedup of 4096
+    lists of 2048 (~25% repeats).  Eight
     independent input sets (about 300 MB of rows and 270 MB of lists) rotate
     through the timed launches so they do not sit in the 256 MB MALL.  Average
     launch time of a HIP graph of 16 launches replayed 5 times between events."""
@@ -455,6 +456,7 @@ def run_write_compaction(dev):
         return e0.elapsed_time(e1) / (LAUNCHES * REPS)
 
     w_ms = timed(lambda i: kv4.quant_write(rows[i], slots, pool))
+    m_ms = timed(lambda i: kv4.quant_write_mse(rows[i], slots, pool))
     d_ms = timed(lambda i: kv4.dedup_compact(lists[i], out_idx=out_idx, out_count=out_cnt))
     w_bytes = spec.n_tokens * (576 * 4 + 4 + 352)
     d_bytes = spec.n_lists * (2 * spec.list_len * 4 + 4)
@@ -462,6 +464,9 @@ def run_write_compaction(dev):
             "write": {"tokens": spec.n_tokens, "us": round(w_ms * 1e3, 2), "algorithmic_bytes": w_bytes,
                       "gbs": round(w_bytes / (w_ms * 1e-3) / 1e9, 1),
                       "hbm_frac": round(w_bytes / (w_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "write_mse": {"tokens": spec.n_tokens, "us": round(m_ms * 1e3, 2), "algorithmic_bytes": w_bytes,
+                          "gbs": round(w_bytes / (m_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(w_bytes / (m_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "dedup": {"lists": spec.n_lists, "k": spec.list_len, "us": round(d_ms * 1e3, 2), "algorithmic_bytes": d_bytes,
                       "gbs": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
                       "hbm_frac": round(d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}

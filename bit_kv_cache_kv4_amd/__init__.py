@@ -22,9 +22,9 @@ import torch
 __all__ = [
     "Kv4Error", "ROW_BYTES", "ROW_BYTES_ROPE_FREE", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
     "library_path", "load", "version", "last_error",
-    "quant_write", "dedup_compact", "write_and_dedup", "global_compact", "global_compact_workspace", "sparse_mla_decode", "sparse_mla_decode_partial",
-    "sparse_mla_decode_splits", "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill",
-    "gather_dequant",
+    "quant_write", "quant_write_mse", "dedup_compact", "write_and_dedup", "global_compact",
+    "global_compact_workspace", "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_splits",
+    "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill", "gather_dequant",
 ]
 
 LATENT, ROPE, DIM, ROW_BYTES = 512, 64, 576, 352
@@ -87,6 +87,7 @@ def load():
     L.kv4_attn_args_size.argtypes, L.kv4_attn_args_size.restype = [], sz
     L.kv4_quant_write.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
     L.kv4_quant_write_rope_free.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp]
+    L.kv4_quant_write_mse.argtypes = [vp, i64, vp, i64, vp, i64, i32, vp, vp]
     L.kv4_dedup_compact.argtypes = [vp, i64, i32, i64, vp, vp, vp]
     L.kv4_write_and_dedup.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i32, i64, vp, vp, vp]
     L.kv4_global_compact_workspace.argtypes, L.kv4_global_compact_workspace.restype = [pa], sz
@@ -170,6 +171,16 @@ def quant_write(kv, slots, pool, err_word=None, stream=None) -> None:
     _check_write_args(kv, slots, pool, err_word)
     _check(load().kv4_quant_write(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
                                   _ptr(err_word), _stream(stream, kv.device)))
+
+
+def quant_write_mse(kv, slots, pool, err_word=None, stream=None) -> None:
+    """kv4_quant_write_mse: quant_write with MSE-searched block scales; the row format
+    (352-byte rows from 576 values, or 288-byte rope-free rows from 512) follows the pool."""
+    rope_free = pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE
+    _check_write_args(kv, slots, pool, err_word, rope_free=rope_free)
+    _check(load().kv4_quant_write_mse(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
+                                      _ROW_ROPE_FREE if rope_free else _ROW_ROPE, _ptr(err_word),
+                                      _stream(stream, kv.device)))
 
 
 # ------------------------------------------------------------------ dedup

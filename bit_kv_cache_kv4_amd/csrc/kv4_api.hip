@@ -219,6 +219,21 @@ kv4_status kv4_quant_write_rope_free(const float *kv, int64_t kv_row_stride, con
                       "quant_write_rope_free launch");
 }
 
+kv4_status kv4_quant_write_mse(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                               uint8_t *pool, int64_t n_slots, kv4_row_format row_format, uint32_t *err_word,
+                               void *stream) {
+    if (row_format != KV4_ROW_ROPE && row_format != KV4_ROW_ROPE_FREE)
+        return fail(KV4_ERR_SHAPE, "row_format = %d; need KV4_ROW_ROPE or KV4_ROW_ROPE_FREE", (int)row_format);
+    const bool rope = row_format == KV4_ROW_ROPE;
+    bool work = false;
+    const kv4_status st =
+        check_quant_write(kv, kv_row_stride, slots, n_tokens, pool, n_slots, &work, rope ? KV4_DIM : KV4_LATENT);
+    if (st != KV4_OK || !work) return st;
+    return hip_status(kv4::launch_quant_write_mse(kv, kv_row_stride, slots, n_tokens, pool, pool ? n_slots : 0, rope,
+                                                  err_word, (hipStream_t)stream),
+                      "quant_write_mse launch");
+}
+
 kv4_status kv4_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride, int32_t *out_idx,
                              int32_t *out_count, void *stream) {
     bool work = false;

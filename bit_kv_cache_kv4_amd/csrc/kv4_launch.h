@@ -16,6 +16,12 @@ hipError_t launch_quant_write_rope_free(const float *kv, int64_t kv_row_stride, 
                                         int64_t n_tokens, uint8_t *pool, int64_t n_slots, uint32_t *err_word,
                                         hipStream_t stream);
 
+// the same with MSE-searched block scales (kv4_quant_mse.hip); rope: 352-byte
+// rows from 576 values, else 288-byte rows from 512
+hipError_t launch_quant_write_mse(const float *kv, int64_t kv_row_stride, const int32_t *slots, int64_t n_tokens,
+                                  uint8_t *pool, int64_t n_slots, bool rope, uint32_t *err_word,
+                                  hipStream_t stream);
+
 hipError_t launch_dedup_compact(const int32_t *idx, int64_t n_lists, int32_t k, int64_t idx_row_stride,
                                 int32_t *out_idx, int32_t *out_count, hipStream_t stream);
 

@@ -38,6 +38,32 @@ __device__ __forceinline__ uint32_t e2m1x8_hw(const float y[8]) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
 }
 
+// E2M1 codes (code i in bits 4i..4i+3) of the eight fp32 quotients x[i] / d,
+// d > 0, without eight divisions: with rd the hardware reciprocal of d (within
+// 1 ulp), q = x * rd is within 2^-22 of the rounded quotient, relatively, so
+// when q nudged 2^-20 down and up gives the same codes, so does the quotient
+// (the conversion is monotone in magnitude and the nudge spans that gap).
+// Otherwise (a quotient at or next to a rounding midpoint), or with a NaN
+// present, the lane divides.
+__device__ __forceinline__ uint32_t e2m1x8_of_quotients(const float x[8], float d) {
+    const float rd = __builtin_amdgcn_rcpf(d);
+    float lo[8], hi[8], sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = x[i] * rd;
+        lo[i] = q * (1.0f - 0x1p-20f);
+        hi[i] = q * (1.0f + 0x1p-20f);
+        sum += x[i];
+    }
+    uint32_t word = e2m1x8_hw(lo);
+    if (word != e2m1x8_hw(hi) || sum != sum) {
+        word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[i] / d) << (4 * i);
+    }
+    return word;
+}
+
 // Row `row` written by one wavefront (lane = its lane index).  ROPE: the
 // 352-byte row from 576 values; otherwise the 288-byte rope-free row (codes
 // and scales) from 512.
@@ -67,31 +93,7 @@ __device__ __forceinline__ void quant_write_row(const float *__restrict__ kv, in
 
     const uint32_t s = e4m3_encode_hw(amax / 6.0f);        // IEEE fp32 division; amax / 6 is never NaN
     const float d = e4m3_pos_to_float(s);
-    uint32_t word = 0;
-    if (d != 0.0f) {
-        // Codes of the fp32 quotients x / d without eight divisions: with rd
-        // the hardware reciprocal of d (within 1 ulp), q = x * rd is within 2^-22
-        // of the rounded quotient, relatively, so when q nudged 2^-20 down and
-        // up gives the same codes, so does the quotient (the conversion is
-        // monotone in magnitude and the nudge spans that gap).  Otherwise (a
-        // quotient at or next to a rounding midpoint), or with a NaN present,
-        // the lane divides.
-        const float rd = __builtin_amdgcn_rcpf(d);
-        float lo[8], hi[8], sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float q = x[i] * rd;
-            lo[i] = q * (1.0f - 0x1p-20f);
-            hi[i] = q * (1.0f + 0x1p-20f);
-            sum += x[i];
-        }
-        word = e2m1x8_hw(lo);
-        if (word != e2m1x8_hw(hi) || sum != sum) {
-            word = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) word |= e2m1_encode(x[i] / d) << (4 * i);
-        }
-    }
+    const uint32_t word = d != 0.0f ? e2m1x8_of_quotients(x, d) : 0u;
     const uint32_t rc = e4m3_encode_hw(r);
 
     // Lane m < 8 gathers the scales of blocks 4m..4m+3 (held by lanes

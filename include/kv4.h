@@ -120,6 +120,26 @@ kv4_status kv4_quant_write_rope_free(const float *kv, int64_t kv_row_stride, con
                                      void *stream);
 
 /*
+ * kv4_quant_write with MSE-searched block scales (README, "4-bit KV cache":
+ * the DeepSeek V4 Pro pools quantize with an MSE-searched scale).  Per
+ * latent block, every finite non-negative E4M3 scale d is a candidate; its
+ * error is the fp32 sum over the 16 values, in index order and one fused
+ * multiply-add each, of (x - c d)^2 with c the E2M1 code of the fp32
+ * quotient x / d (all codes zero when d = 0).  The amax/6 scale of
+ * kv4_quant_write stays unless a candidate is strictly better; ties among
+ * better candidates go to the smallest code.  Codes are then those of the
+ * chosen scale, and rope bytes are as in kv4_quant_write.  A block holding a
+ * NaN or an infinity keeps the amax/6 scale.
+ *   row_format    KV4_ROW_ROPE: kv rows of 576 values, pool [n_slots, 352];
+ *                 KV4_ROW_ROPE_FREE: kv rows of 512, pool [n_slots, 288].
+ * Everything else (slots, pads, flags, alignment, errors) as kv4_quant_write,
+ * plus KV4_ERR_SHAPE for an unknown row_format.
+ */
+kv4_status kv4_quant_write_mse(const float *kv, int64_t kv_row_stride, const int32_t *slots,
+                               int64_t n_tokens, uint8_t *pool, int64_t n_slots, kv4_row_format row_format,
+                               uint32_t *err_word, void *stream);
+
+/*
  * Dedup compaction of top-k lists (README, "4-bit KV cache": dedup
  * compaction).  For each list l in [0, n_lists), independently: walk
  * idx[l * idx_row_stride + 0..k-1] in order, keep the first occurrence of

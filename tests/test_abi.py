@@ -135,6 +135,22 @@ def test_quant_write_argument_checks():
     assert f(V(0x10), 576, V(0x10), 4, None, 8, None, None) == 1
 
 
+def test_quant_write_mse_argument_checks():
+    lib = kv4.load()
+    f = lib.kv4_quant_write_mse
+    V = ctypes.c_void_p
+    assert f(None, 576, None, 0, None, 0, 0, None, None) == 0              # nothing to do
+    assert f(V(0x10), 576, V(0x10), 4, V(0x20), 8, 2, None, None) == 2    # unknown row format
+    assert f(V(0x10), 576, V(0x10), 4, V(0x20), 8, -1, None, None) == 2
+    assert f(V(0x10), 575, V(0x10), 4, V(0x20), 8, 0, None, None) == 3
+    assert f(V(0x10), 512, V(0x10), 4, V(0x20), 8, 0, None, None) == 3    # 352-byte rows need 576 values
+    assert f(V(0x10), 511, V(0x10), 4, V(0x20), 8, 1, None, None) == 3
+    assert f(V(0x18), 512, V(0x10), 4, V(0x20), 8, 1, None, None) == 3
+    assert f(None, 576, V(0x10), 4, V(0x20), 8, 0, None, None) == 1
+    assert f(V(0x10), 576, V(0x10), 4, V(0x20), 8, 9, None, None) == 2
+    assert b"row_format" in lib.kv4_last_error()
+
+
 def test_dedup_argument_checks():
     lib = kv4.load()
     f = lib.kv4_dedup_compact
