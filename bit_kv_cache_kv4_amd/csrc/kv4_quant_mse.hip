@@ -13,16 +13,16 @@
 // x / d = (x / (1 + m/8)) 2^-e exactly whenever that is a normal float; where
 // it is not (a quotient under 2^-117 or past the fp32 range) both forms give
 // the same code (zero, or saturation at 6).  So a lane divides its values by
-// the eight mantissas once and scales by a power of two per exponent.
+// the eight mantissas once, and the conversion to FP4 applies 2^-e.
 // Candidates that cannot be chosen are not evaluated:
 //  * below: when 6d <= amax, the block's largest value errs by at least
 //    amax - 6d under d, and an fp32 sum of squares never falls below one of
 //    its terms, so fl(fl(amax - 6d)^2) >= the amax/6 error rules d out;
 //  * above: once amax / 2^e < 1/4 every code is zero for every mantissa and
 //    the error no longer depends on d, so only the smallest such code, which
-//    lies at or below exponent e, can be chosen.
-// The exponents a wavefront visits are taken relative to each lane's amax/6
-// exponent, so lanes of rows of very different magnitude share iterations.
+//    lies at or below exponent e, can be chosen; and a d that codes a set of
+//    the smallest values as zero while their squares alone reach the amax/6
+//    error is ruled out too.
 #include "kv4_quant_impl.h"
 #include "kv4_launch.h"
 
@@ -86,10 +86,51 @@ __device__ __forceinline__ int e4m3_code_exponent(uint32_t k) {
     return (31 - __builtin_clz(k)) - 9;
 }
 
-__device__ __forceinline__ int wave_min(int v) {
+// The correctly rounded quotient x / mult for mult = 1 + m/8 from the
+// rounded reciprocal r and one fused correction: q0 = x r, the residual
+// x - q0 mult is exact, and q0 + residual r rounds to the same float as the
+// quotient for every x in [1, 2) and each of the eight divisors (checked
+// exhaustively), hence for every normal x, since each step commutes with
+// scaling by powers of two.  The sign is restored for zeros (+0 from the
+// residual).  For subnormal x the result can differ from the quotient, but
+// both code as zero of x's sign at every candidate scale.
+__device__ __forceinline__ float quotient(float x, float mult, float r) {
+    const float q0 = x * r;
+    const float rem = __builtin_fmaf(-q0, mult, x);
+    return __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
+}
+
+// E2M1 codes of q[i] / scale for a power-of-two scale (gfx950's fp32 -> FP4
+// conversion divides by the scale exactly before rounding, so this equals the
+// codes of the products q[i] * (1 / scale) at scale 1).
+__device__ __forceinline__ uint32_t e2m1x8_div_pow2(const float q[8], float scale) {
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], scale, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], scale, 3);
+}
+
+// Ascending sort of 16 values (Batcher's odd-even merge network; all indices
+// are compile-time constants, so the values stay in registers).
+__device__ __forceinline__ void sort16(float v[16]) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
+    for (int p = 1; p < 16; p <<= 1) {
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+            for (int j = k % p; j + k < 16; j += 2 * k) {
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    const int lo = i + j, hi = i + j + k;
+                    if (hi < 16 && lo / (2 * p) == hi / (2 * p)) {
+                        const float a = v[lo], b = v[hi];
+                        v[lo] = __builtin_fminf(a, b);
+                        v[hi] = __builtin_fmaxf(a, b);
+                    }
+                }
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ int wave_max(int v) {
@@ -160,50 +201,82 @@ __global__ __launch_bounds__(kMseThreads) void quant_write_mse_kernel(const floa
         }
     }
 
-    // Exponents to visit, relative to the amax/6 exponent.  Above: e_hi with
-    // amax < 2^(e_hi - 2).  Below: under e_lo, 6d <= (amax - 1.01 sqrt(err0)) / 8
-    // for every mantissa, which leaves amax - 6d far enough above sqrt(err0)
-    // (rounding included) that the exact test in the loop would reject d.
-    const int e0 = k0 ? e4m3_code_exponent(k0) : -9;
-    int e_hi = -100, dlo = 1 << 20, dhi = -(1 << 20);
+    // Candidates ruled out without evaluating them (each test is exact):
+    //  * 6d <= amax and fl(fl(amax - 6d)^2) >= err0 (the largest value's error);
+    //  * d >= 4a, with a the least magnitude whose values up to it have squares
+    //    summing to err0 or more (with margin for fp32 rounding): d codes all
+    //    of them as zero, so its error sum holds those squares unchanged;
+    //  * exponents from e_hi on (amax < 2^(e_hi - 2)) when no such a exists:
+    //    every code is zero there and the error no longer depends on d, so
+    //    only the smallest such code, at or below e_hi, can be chosen.
+    // For a fixed mantissa the survivors are one run of exponents, since the
+    // first test rules out a prefix and the others a suffix; each lane walks
+    // its own run, so a wavefront iterates over the longest run, not over the
+    // union of its lanes' exponent ranges.
+    int e_up = -100;
+    float four_a = __builtin_inff();
     if (search) {
         int E;
         __builtin_frexpf(amax, &E);                          // amax = f 2^E, f in [0.5, 1)
-        e_hi = min(E + 2, 8);
-        int e_lo = -9;
+        e_up = min(E + 2, 8);
+        float mag[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mag[i] = __builtin_fabsf(x[i]);
+        sort16(mag);
+        const float need = err0 * (1.0f + 0x1p-16f);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc = __builtin_fmaf(mag[i], mag[i], acc);
+            if (acc >= need && four_a == __builtin_inff()) four_a = 4.0f * mag[i];
+        }
+        if (four_a < __builtin_inff()) {
+            int F;
+            __builtin_frexpf(four_a, &F);                    // 4a < 2^F: every d with e >= F is >= 4a
+            e_up = min(e_up, F - 1);
+        }
+    }
+    // a lower start for the runs: below e_lo, 6d <= (amax - 1.01 sqrt(err0)) / 8
+    // for every mantissa, far enough under amax - sqrt(err0) that the first
+    // test rules d out (rounding included)
+    int e_lo = -9;
+    if (search) {
         const float t = (amax - 1.01f * __builtin_sqrtf(err0)) * (1.0f / 11.25f);
         if (t > 0.0f) {
             int Et;
             __builtin_frexpf(t, &Et);                        // t >= 2^(Et - 1)
             e_lo = max(-9, Et - 3);
         }
-        dlo = e_lo - e0;
-        dhi = e_hi - e0;
     }
-    dlo = wave_min(dlo);
-    dhi = wave_max(dhi);
 
-    if (dlo <= dhi) {
+    if (__builtin_amdgcn_ballot_w64(search)) {
         for (int m = 0; m < 8; ++m) {
             const float mult = 1.0f + 0.125f * (float)m;
+            const float r = 1.0f / mult;                     // rounded reciprocal
+            // this lane's run [e_a, e_b] for mantissa m
+            int e_a = e_lo, e_b = e_up;
+            if (search) {
+                while (e_a <= e_b) {
+                    const float six_d = 6.0f * __builtin_ldexpf(mult, e_a);
+                    const float gap = amax - six_d;
+                    if (!(six_d <= amax && gap * gap >= err0)) break;
+                    ++e_a;
+                }
+                while (e_b >= e_a && four_a <= __builtin_ldexpf(mult, e_b)) --e_b;
+            }
+            const int n_run = search ? max(e_b - e_a + 1, 0) : 0;
+            const int n_it = wave_max(n_run);
+            if (n_it == 0) continue;
             float q[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) q[i] = x[i] / mult;      // IEEE division
-            for (int dl = dlo; dl <= dhi; ++dl) {
-                const int e = e0 + dl;
-                const int k = (search && e <= e_hi) ? e4m3_candidate_code(m, e) : -1;
+            for (int i = 0; i < 16; ++i) q[i] = quotient(x[i], mult, r);
+            for (int it = 0; it < n_it; ++it) {
+                const int e = e_a + it;
+                const int k = it < n_run ? e4m3_candidate_code(m, e) : -1;
                 if (k < 0) continue;
                 const float d = __builtin_ldexpf(mult, e);
-                const float six_d = 6.0f * d;
-                if (six_d <= amax) {
-                    const float gap = amax - six_d;
-                    if (gap * gap >= err0) continue;
-                }
-                const float p = __builtin_ldexpf(1.0f, -e);
-                float y[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) y[i] = q[i] * p;
-                const uint32_t w0 = e2m1x8_hw(y), w1 = e2m1x8_hw(y + 8);
+                const float scale = __builtin_ldexpf(1.0f, e);
+                const uint32_t w0 = e2m1x8_div_pow2(q, scale), w1 = e2m1x8_div_pow2(q + 8, scale);
                 const float err = block_sq_error(x, w0, w1, d);
                 if (err < best_err || (err == best_err && best_k != (int)k0 && k < best_k)) {
                     best_err = err;
