@@ -120,7 +120,7 @@ def prefill_flops(n_rows, n_heads, k):
     return 2.0 * n_rows * n_heads * k * (576 + 512)
 
 
-ATTN_SOURCES = ("kv4_attn.hip", "kv4_device.h", "kv4_launch.h")   # what the attention kernel is built from
+ATTN_SOURCES = ("kv4_attn.hip", "kv4_attn.h", "kv4_device.h")   # what the attention kernel is built from
 
 
 def kernel_source_digest():

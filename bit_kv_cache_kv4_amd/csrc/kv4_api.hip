@@ -385,7 +385,7 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
 
 size_t kv4_global_compact_workspace(const kv4_attn_args *a) {
     if (check_attn(a, false) != KV4_OK) return 0;
-    return kv4::compact_workspace(a->pool ? a->n_slots : 0, (int64_t)a->n_rows * a->k).bytes;
+    return kv4::compact_workspace(a->pool ? a->n_slots : 0, a->n_rows, a->k).bytes;
 }
 
 kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cpool_rows, int32_t *out_idx,
@@ -396,7 +396,9 @@ kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cp
     const int64_t n_slots = a->pool ? a->n_slots : 0;
     if (n_slots > 0x7FFFFFFF) return fail(KV4_ERR_UNSUPPORTED, "n_slots = %lld; at most 2^31 - 1", (long long)n_slots);
     const int64_t n_entries = (int64_t)a->n_rows * a->k;
-    const kv4::CompactWorkspace w = kv4::compact_workspace(n_slots, n_entries);
+    if ((int64_t)a->n_rows * ((a->k + 255) / 256) + (n_slots + 8191) / 8192 > 0x7FFFFFFF)
+        return fail(KV4_ERR_UNSUPPORTED, "n_rows * ceil(k / 256) too large for one launch");
+    const kv4::CompactWorkspace w = kv4::compact_workspace(n_slots, a->n_rows, a->k);
     if (n_entries > 0 && !out_idx) return fail(KV4_ERR_NULL, "out_idx is NULL");
     if (cpool_rows < w.max_rows)
         return fail(KV4_ERR_SHAPE, "cpool has %lld rows; min(n_slots, n_rows * k) = %lld needed", (long long)cpool_rows,

@@ -43,8 +43,8 @@
 // score k-steps per half instead of 18 and no rope to gather or decode; it
 // keeps the same slot schedule and LDS layout (the last 8 chunks of each K
 // tile unused).
+#include "kv4_attn.h"
 #include "kv4_device.h"
-#include "kv4_launch.h"
 
 #include <type_traits>
 
