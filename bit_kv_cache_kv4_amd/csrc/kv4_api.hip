@@ -55,6 +55,7 @@ kv4_status check_attn(const kv4_attn_args *a, bool need_out) {
     if (a->n_heads < 16 || a->n_heads > 128 || a->n_heads % 16)
         return fail(KV4_ERR_UNSUPPORTED, "n_heads = %d; supported: a multiple of 16 in [16, 128]", a->n_heads);
     if (a->k < 0) return fail(KV4_ERR_SHAPE, "k = %d < 0", a->k);
+    if (a->k > KV4_MAX_K) return fail(KV4_ERR_UNSUPPORTED, "k = %d > %d", a->k, KV4_MAX_K);
     if (a->n_slots < 0) return fail(KV4_ERR_SHAPE, "n_slots < 0");
     if (a->n_rows == 0) return ok();
     if (!a->q) return fail(KV4_ERR_NULL, "q is NULL");

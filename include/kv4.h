@@ -54,6 +54,7 @@ extern "C" {
 
 #define KV4_MAX_DEDUP_K 4096   /* longest list kv4_dedup_compact accepts */
 #define KV4_MAX_SPLITS 64      /* most splits kv4_sparse_mla_decode uses */
+#define KV4_MAX_K (1 << 30)    /* longest list the attention and compaction entry points accept */
 
 typedef enum {
     KV4_OK = 0,
@@ -204,7 +205,7 @@ typedef struct kv4_attn_args {
     const int32_t *row_req;    /* device [n_rows], nullable: page-table row of each query row */
     const int32_t *topk;       /* device [n_rows, >= k] */
     int64_t topk_row_stride;   /* elements, >= k */
-    int32_t k;                 /* list length, >= 0 */
+    int32_t k;                 /* list length, 0 <= k <= KV4_MAX_K */
     float sm_scale;            /* softmax scale, e.g. 1/sqrt(576) */
     float *out;                /* device [n_rows, n_heads, 512] fp32; 16-byte aligned */
     int64_t out_row_stride;    /* elements, >= n_heads * 512, multiple of 4 */

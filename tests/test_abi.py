@@ -71,6 +71,7 @@ BAD_ARGS = [
     (dict(n_heads=20), 4, "n_heads"),
     (dict(n_heads=256), 4, "n_heads"),
     (dict(k=-1), 2, "k"),
+    (dict(k=(1 << 30) + 1, topk_row_stride=(1 << 30) + 1), 4, "k"),
     (dict(q=None), 1, "q is NULL"),
     (dict(topk=None), 1, "topk"),
     (dict(out=None), 1, "out"),
