@@ -41,10 +41,13 @@ def test_compact_invalid_entries_and_missing_requests(row_bytes):
     _both(pool, topk, pt, row_req)
 
 
-@pytest.mark.parametrize("n_slots,R,k", [(1000, 1, 5), (1000, 3, 0), (70000, 40, 2048), (1 << 21, 64, 2048)])
+@pytest.mark.parametrize("n_slots,R,k", [(1000, 1, 5), (1000, 3, 0), (70000, 40, 2048), (1 << 21, 64, 2048),
+                                         (400000, 17, 3000), (1000, 1100, 64), (262144, 3, 100)])
 def test_compact_physical_slots(n_slots, R, k):
-    """Lists of physical slots; 2^21 slots take the global-atomic marking,
-    the others the LDS one."""
+    """Lists of physical slots.  2^21 slots take the global-atomic marking;
+    the others the LDS marking, with the rewrite's word table in LDS up to
+    262,144 slots (400,000 slots: marking in LDS, rewrite from global memory);
+    1100 rows give several rows to each of the 512 marking workgroups."""
     g = np.random.default_rng(n_slots + R)
     pool_d = torch.randint(0, 256, (n_slots, 352), dtype=torch.uint8, device=DEV)
     pool_h = pool_d.cpu().numpy()
