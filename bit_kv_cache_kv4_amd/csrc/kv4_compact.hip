@@ -7,14 +7,14 @@
 // lists as physical slots then gathers from |U| contiguous rows instead of
 // scattered ones and equals attention over the original, entry for entry.
 //
-// A bitmap over the pool's slots carries the set: launches mark the entries
+// A bitmap over the pool's slots carries the set.  Launches mark the entries
 // (when the bitmap fits in 64 KB, each workgroup into an LDS copy stored as a
 // partial bitmap, then OR-ed together; otherwise one global atomic per entry
-// into a cleared bitmap), scan it (per
-// word, then per block of 4096 words, then over the blocks), then one launch
-// both lists U and rewrites the entries (a slot's index is its block's base
-// plus its word's base plus the set bits below it in the word), and a last
-// one copies the rows, one 16-byte piece per lane.
+// into a cleared bitmap), scan it (per word, then per block of 4096 words,
+// then over the blocks), list U and rewrite the entries (a slot's index is
+// its block's base plus its word's base plus the set bits below it in the
+// word; for small bitmaps the rewrite is a launch of its own that reads the
+// word table from LDS), and copy the rows, one 16-byte piece per lane.
 #include "kv4_device.h"
 #include "kv4_launch.h"
 
@@ -25,7 +25,7 @@ namespace kv4 {
 constexpr int kCompactThreads = 256;
 constexpr int kScanWords = 4096;                 // bitmap words per scan block
 constexpr int kLdsMarkWords = 16384;             // bitmaps up to 64 KB are marked in LDS first
-constexpr int kMarkThreads = 512;               // LDS marking: lanes per workgroup,
+constexpr int kMarkThreads = 512;                // LDS marking: lanes per workgroup,
 constexpr int kMarkParts = 512;                  // at most this many workgroups (partial bitmaps),
 constexpr int kMarkPer = 32;                     // and entries per lane per round
 constexpr int kEmitPer = 4;                      // entries per lane when rewriting the lists
@@ -374,8 +374,8 @@ CompactWorkspace compact_workspace(int64_t n_slots, int32_t n_rows, int32_t k) {
         w.n_parts = (n_rows + w.rows_per_part - 1) / w.rows_per_part;
     }
     w.bitmap_off = 0;
-    w.word_base_off = up((size_t)w.n_words * 4);
-    w.block_sum_off = w.word_base_off + up((size_t)w.n_words * 8);
+    w.word_info_off = up((size_t)w.n_words * 4);
+    w.block_sum_off = w.word_info_off + up((size_t)w.n_words * 8);
     w.block_base_off = w.block_sum_off + up((size_t)w.n_blocks * 4);
     w.uslots_off = w.block_base_off + up((size_t)w.n_blocks * 4);
     w.parts_off = w.uslots_off + up((size_t)(w.max_rows > 0 ? w.max_rows : 1) * 4);
@@ -387,7 +387,7 @@ hipError_t launch_global_compact(const CompactParams &p, void *workspace, hipStr
     const CompactWorkspace w = compact_workspace(p.n_slots, p.n_rows, p.k);
     char *ws = static_cast<char *>(workspace);
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + w.bitmap_off);
-    uint2 *word_info = reinterpret_cast<uint2 *>(ws + w.word_base_off);
+    uint2 *word_info = reinterpret_cast<uint2 *>(ws + w.word_info_off);
     uint32_t *block_sum = reinterpret_cast<uint32_t *>(ws + w.block_sum_off);
     uint32_t *block_base = reinterpret_cast<uint32_t *>(ws + w.block_base_off);
     int32_t *uslots = reinterpret_cast<int32_t *>(ws + w.uslots_off);

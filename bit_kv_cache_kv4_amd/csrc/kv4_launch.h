@@ -66,13 +66,14 @@ struct CompactParams {
     uint32_t *err_word;
 };
 
-// Workspace layout of the compaction: slot bitmap, per-word and per-block
-// prefixes, the list U of slots and, for bitmaps marked in LDS, one partial
-// bitmap per marking workgroup (each part 256-byte aligned).
+// Workspace layout of the compaction: slot bitmap, per-word bits and prefix
+// (uint2), per-block sums and bases, the list U of slots and, for bitmaps
+// marked in LDS, one partial bitmap per marking workgroup (each part 256-byte
+// aligned).
 struct CompactWorkspace {
     int64_t n_words, n_blocks, max_rows;
     int32_t n_parts, rows_per_part;   // LDS marking: workgroups and the query rows each takes (0: global marking)
-    size_t bitmap_off, word_base_off, block_sum_off, block_base_off, uslots_off, parts_off, bytes;
+    size_t bitmap_off, word_info_off, block_sum_off, block_base_off, uslots_off, parts_off, bytes;
 };
 CompactWorkspace compact_workspace(int64_t n_slots, int32_t n_rows, int32_t k);
 hipError_t launch_global_compact(const CompactParams &p, void *workspace, hipStream_t stream);

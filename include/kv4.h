@@ -301,7 +301,9 @@ kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *sl
  *                 aligned; cpool_rows >= min(n_slots, n_rows * k).
  *   out_idx       device int32 [n_rows, k]; out_count device int32 [1].
  *   workspace     device, >= kv4_global_compact_workspace(a) bytes, 256-byte
- *                 aligned (a bitmap of n_slots bits, prefixes and U).
+ *                 aligned (a bitmap of n_slots bits, per-word prefixes, U
+ *                 and, for pools of at most 2^19 slots, up to 512 partial
+ *                 bitmaps); its contents need no initialisation.
  * Errors: those of kv4_sparse_mla_decode, KV4_ERR_WORKSPACE, and
  * KV4_ERR_UNSUPPORTED for n_slots >= 2^31.
  */
