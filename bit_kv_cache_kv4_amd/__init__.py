@@ -366,11 +366,16 @@ def sparse_mla_prefill(q, pool, topk, sm_scale, page_table=None, row_req=None, p
     return out, lse
 
 
-def _compact_args(pool, topk, page_table, row_req, page_size, err_word):
-    R = topk.shape[0]
+def _unread_q(pool, topk):
+    """A stand-in q for the entry points that do not read it (one row of 16
+    heads, broadcast over the list rows, so nothing of q's size is allocated)."""
     rope_free = pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE
-    dummy_q = torch.empty((R, 16, LATENT if rope_free else DIM), dtype=torch.bfloat16, device=topk.device)
-    return _attn_args(dummy_q, pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
+    return torch.empty((1, 16, LATENT if rope_free else DIM), dtype=torch.bfloat16,
+                       device=topk.device).expand(topk.shape[0], 16, -1)
+
+
+def _compact_args(pool, topk, page_table, row_req, page_size, err_word):
+    return _attn_args(_unread_q(pool, topk), pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
 
 
 def global_compact_workspace(pool, topk, page_table=None, row_req=None, page_size=64) -> int:
@@ -416,8 +421,7 @@ def gather_dequant(pool, topk, page_table=None, row_req=None, page_size=64, err_
     for a rope-free (288-byte) pool."""
     R, k = topk.shape[0], topk.shape[1]
     dim = LATENT if pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE else DIM
-    dummy_q = torch.empty((R, 16, dim), dtype=torch.bfloat16, device=topk.device)
-    a = _attn_args(dummy_q, pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
+    a = _attn_args(_unread_q(pool, topk), pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)
     out = torch.empty((R, k, dim), dtype=torch.float16, device=topk.device)
     slots = torch.empty((R, k), dtype=torch.int32, device=topk.device)
     _check(load().kv4_gather_dequant(ctypes.byref(a), _ptr(out), _ptr(slots), _stream(stream, topk.device)))

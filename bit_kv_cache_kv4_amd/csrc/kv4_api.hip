@@ -43,7 +43,10 @@ int device_cu_count() {
 
 constexpr int kTile = 32;
 
-kv4_status check_attn(const kv4_attn_args *a, bool need_out) {
+// Argument checks shared by the entry points that take kv4_attn_args; with
+// need_q false (the gather and the compaction) q, its strides and n_heads are
+// not used and not checked.
+kv4_status check_attn(const kv4_attn_args *a, bool need_out, bool need_q = true) {
     if (!a) return fail(KV4_ERR_NULL, "args is NULL");
     if (a->struct_size != sizeof(kv4_attn_args))
         return fail(KV4_ERR_SHAPE, "args->struct_size = %u, this library expects %zu", a->struct_size,
@@ -52,25 +55,28 @@ kv4_status check_attn(const kv4_attn_args *a, bool need_out) {
     if (a->row_format != KV4_ROW_ROPE && a->row_format != KV4_ROW_ROPE_FREE)
         return fail(KV4_ERR_SHAPE, "row_format must be KV4_ROW_ROPE or KV4_ROW_ROPE_FREE");
     if (a->n_rows < 0) return fail(KV4_ERR_SHAPE, "n_rows = %d < 0", a->n_rows);
-    if (a->n_heads < 16 || a->n_heads > 128 || a->n_heads % 16)
+    if (need_q && (a->n_heads < 16 || a->n_heads > 128 || a->n_heads % 16))
         return fail(KV4_ERR_UNSUPPORTED, "n_heads = %d; supported: a multiple of 16 in [16, 128]", a->n_heads);
     if (a->k < 0) return fail(KV4_ERR_SHAPE, "k = %d < 0", a->k);
     if (a->k > KV4_MAX_K) return fail(KV4_ERR_UNSUPPORTED, "k = %d > %d", a->k, KV4_MAX_K);
     if (a->n_slots < 0) return fail(KV4_ERR_SHAPE, "n_slots < 0");
     if (a->n_rows == 0) return ok();
-    if (!a->q) return fail(KV4_ERR_NULL, "q is NULL");
+    if (need_q && !a->q) return fail(KV4_ERR_NULL, "q is NULL");
     if (a->k > 0 && !a->topk) return fail(KV4_ERR_NULL, "topk is NULL");
     if (a->k > 0 && !a->pool && a->n_slots > 0) return fail(KV4_ERR_NULL, "pool is NULL");
     if (need_out && !a->out) return fail(KV4_ERR_NULL, "out is NULL");
-    const int64_t vec = a->q_dtype == KV4_BF16 ? 8 : 4;
-    if (!aligned(a->q, 16)) return fail(KV4_ERR_ALIGN, "q must be 16-byte aligned");
-    const int64_t dim = a->row_format == KV4_ROW_ROPE_FREE ? KV4_LATENT : KV4_DIM;
-    if (a->q_head_stride < dim || a->q_head_stride % vec)
-        return fail(KV4_ERR_ALIGN, "q_head_stride = %lld; need >= %lld and a multiple of %lld", (long long)a->q_head_stride,
-                    (long long)dim, (long long)vec);
-    if (a->q_row_stride < 0 || a->q_row_stride % vec || (a->n_rows > 1 && a->q_row_stride < a->q_head_stride * a->n_heads))
-        return fail(KV4_ERR_ALIGN, "q_row_stride = %lld; need >= n_heads * q_head_stride and a multiple of %lld",
-                    (long long)a->q_row_stride, (long long)vec);
+    if (need_q) {
+        const int64_t vec = a->q_dtype == KV4_BF16 ? 8 : 4;
+        if (!aligned(a->q, 16)) return fail(KV4_ERR_ALIGN, "q must be 16-byte aligned");
+        const int64_t dim = a->row_format == KV4_ROW_ROPE_FREE ? KV4_LATENT : KV4_DIM;
+        if (a->q_head_stride < dim || a->q_head_stride % vec)
+            return fail(KV4_ERR_ALIGN, "q_head_stride = %lld; need >= %lld and a multiple of %lld",
+                        (long long)a->q_head_stride, (long long)dim, (long long)vec);
+        if (a->q_row_stride < 0 || a->q_row_stride % vec ||
+            (a->n_rows > 1 && a->q_row_stride < a->q_head_stride * a->n_heads))
+            return fail(KV4_ERR_ALIGN, "q_row_stride = %lld; need >= n_heads * q_head_stride and a multiple of %lld",
+                        (long long)a->q_row_stride, (long long)vec);
+    }
     if (a->pool && !aligned(a->pool, 16)) return fail(KV4_ERR_ALIGN, "pool must be 16-byte aligned");
     if (a->topk_row_stride < a->k) return fail(KV4_ERR_SHAPE, "topk_row_stride < k");
     if (a->page_table) {
@@ -385,13 +391,13 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
 }
 
 size_t kv4_global_compact_workspace(const kv4_attn_args *a) {
-    if (check_attn(a, false) != KV4_OK) return 0;
+    if (check_attn(a, false, false) != KV4_OK) return 0;
     return kv4::compact_workspace(a->pool ? a->n_slots : 0, a->n_rows, a->k).bytes;
 }
 
 kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cpool_rows, int32_t *out_idx,
                               int32_t *out_count, void *workspace, size_t workspace_bytes, void *stream) {
-    const kv4_status st = check_attn(a, false);
+    const kv4_status st = check_attn(a, false, false);
     if (st != KV4_OK) return st;
     if (!out_count) return fail(KV4_ERR_NULL, "out_count is NULL");
     const int64_t n_slots = a->pool ? a->n_slots : 0;
@@ -431,7 +437,7 @@ kv4_status kv4_global_compact(const kv4_attn_args *a, uint8_t *cpool, int64_t cp
 }
 
 kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *slots_out, void *stream) {
-    const kv4_status st = check_attn(a, false);
+    const kv4_status st = check_attn(a, false, false);
     if (st != KV4_OK) return st;
     if (a->n_rows == 0 || a->k == 0) return ok();
     if (!out) return fail(KV4_ERR_NULL, "out is NULL");

@@ -280,7 +280,8 @@ kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t 
  * themselves.
  *   out           device [n_rows, k, D] uint16 (fp16 bits), 16-byte aligned.
  *   slots_out     device [n_rows, k] int32, nullable.
- * a->q, a->out and a->lse are ignored.  Errors: as kv4_sparse_mla_decode.
+ * a->q, a->q_dtype, its strides, a->n_heads, a->out and a->lse are ignored (q
+ * may be NULL).  Errors: as kv4_sparse_mla_decode.
  */
 kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *slots_out, void *stream);
 
@@ -295,8 +296,8 @@ kv4_status kv4_gather_dequant(const kv4_attn_args *a, uint16_t *out, int32_t *sl
  * pool = cpool, page_table = NULL and topk = out_idx equals attention over
  * the original arguments, entry for entry; the rows it gathers are |U|
  * contiguous ones.
- *   a             the attention arguments (q must pass the argument checks
- *                 but is not read; out and lse are ignored).
+ *   a             the attention arguments; q, q_dtype, its strides, n_heads,
+ *                 sm_scale, out and lse are ignored (q may be NULL).
  *   cpool         device [cpool_rows, row bytes of a->row_format], 16-byte
  *                 aligned; cpool_rows >= min(n_slots, n_rows * k).
  *   out_idx       device int32 [n_rows, k]; out_count device int32 [1].

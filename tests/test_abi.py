@@ -200,6 +200,14 @@ def test_global_compact_argument_checks():
     assert lib.kv4_global_compact_workspace(ctypes.byref(a2)) == need
     a3 = _args(row_format=2)
     assert lib.kv4_global_compact_workspace(ctypes.byref(a3)) == 0
+    # q, its strides and n_heads are not read by the compaction or the gather
+    a4 = _args(q=None, q_row_stride=0, q_head_stride=0, n_heads=0)
+    assert lib.kv4_global_compact_workspace(ctypes.byref(a4)) == need
+    assert f(ctypes.byref(a4), V(0x10000), 32, V(0x20000), None, V(0x100000), need, None) == 1
+    assert "out_count" in kv4.last_error()
+    assert lib.kv4_gather_dequant(ctypes.byref(a4), None, None, None) == 1
+    assert "out" in kv4.last_error()
+    assert lib.kv4_sparse_mla_decode_splits(ctypes.byref(a4)) < 0      # attention still needs q
 
 
 def test_merge_argument_checks():
