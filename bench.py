@@ -196,7 +196,7 @@ def main():
     pool, pt, sets = wl["pool"], wl["pt"], wl["sets"]
     H, R, K = spec.n_heads, spec.n_req, spec.k
     S = args.splits or kv4.sparse_mla_decode_splits(sets[0]["q"], pool, sets[0]["topk"], page_table=pt)
-    part_o = torch.empty((S, R, H, 512), dtype=torch.float32, device=dev)
+    part_o = torch.empty((S, R, H, 512), dtype=torch.float16, device=dev)   # as decode's workspace holds them
     part_lse = torch.empty((S, R, H), dtype=torch.float32, device=dev)
     out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)

@@ -96,11 +96,14 @@ def load():
     L.kv4_sparse_mla_decode_workspace.argtypes, L.kv4_sparse_mla_decode_workspace.restype = [pa, i32], sz
     L.kv4_sparse_mla_decode.argtypes = [pa, i32, vp, sz, vp]
     L.kv4_sparse_mla_decode_partial.argtypes = [pa, i32, vp, vp, vp]
+    L.kv4_sparse_mla_decode_partial_f16.argtypes = [pa, i32, vp, vp, vp]
     L.kv4_merge_states.argtypes = [vp, vp, i32, i64, i32, vp, i64, vp, vp]
+    L.kv4_merge_states_f16.argtypes = [vp, vp, i32, i64, i32, vp, i64, vp, vp]
     L.kv4_sparse_mla_prefill.argtypes = [pa, vp]
     L.kv4_gather_dequant.argtypes = [pa, vp, vp, vp]
     for f in ("kv4_quant_write", "kv4_dedup_compact", "kv4_sparse_mla_decode", "kv4_sparse_mla_decode_partial",
-              "kv4_merge_states", "kv4_sparse_mla_prefill", "kv4_gather_dequant"):
+              "kv4_sparse_mla_decode_partial_f16", "kv4_merge_states", "kv4_merge_states_f16",
+              "kv4_sparse_mla_prefill", "kv4_gather_dequant"):
         getattr(L, f).restype = ctypes.c_int
     if L.kv4_attn_args_size() != ctypes.sizeof(AttnArgs):
         raise Kv4Error(2, "kv4_attn_args layout mismatch: library %d bytes, binding %d"
@@ -318,27 +321,31 @@ def sparse_mla_decode(q, pool, topk, sm_scale, page_table=None, row_req=None, pa
 
 
 def sparse_mla_decode_partial(q, pool, topk, sm_scale, num_splits, page_table=None, row_req=None, page_size=64,
-                              part_o=None, part_lse=None, err_word=None, stream=None):
-    """kv4_sparse_mla_decode_partial; returns (part_o [S, R, H, 512], part_lse [S, R, H])."""
+                              part_o=None, part_lse=None, err_word=None, stream=None, parts_dtype=torch.float32):
+    """kv4_sparse_mla_decode_partial (fp32 parts) or kv4_sparse_mla_decode_partial_f16 (fp16 parts, chosen by
+    part_o's dtype, else by parts_dtype); returns (part_o [S, R, H, 512], part_lse [S, R, H])."""
     R, H = q.shape[0], q.shape[1]
     if part_o is None:
-        part_o = torch.empty((num_splits, R, H, LATENT), dtype=torch.float32, device=q.device)
+        part_o = torch.empty((num_splits, R, H, LATENT), dtype=parts_dtype, device=q.device)
     if part_lse is None:
         part_lse = torch.empty((num_splits, R, H), dtype=torch.float32, device=q.device)
-    _need(part_o, "part_o", torch.float32, q.device)
+    f16 = part_o.dtype == torch.float16
+    _need(part_o, "part_o", torch.float16 if f16 else torch.float32, q.device)
     _need(part_lse, "part_lse", torch.float32, q.device)
     if tuple(part_o.shape) != (num_splits, R, H, LATENT) or not part_o.is_contiguous() or \
             tuple(part_lse.shape) != (num_splits, R, H) or not part_lse.is_contiguous():
         raise ValueError("part_o must be contiguous [S, R, H, 512] and part_lse [S, R, H]")
     a = _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, None, None, err_word)
-    _check(load().kv4_sparse_mla_decode_partial(ctypes.byref(a), int(num_splits), _ptr(part_o), _ptr(part_lse),
-                                                _stream(stream, q.device)))
+    fn = load().kv4_sparse_mla_decode_partial_f16 if f16 else load().kv4_sparse_mla_decode_partial
+    _check(fn(ctypes.byref(a), int(num_splits), _ptr(part_o), _ptr(part_lse), _stream(stream, q.device)))
     return part_o, part_lse
 
 
 def merge_states(part_o, part_lse, out=None, lse=None, stream=None):
-    """kv4_merge_states over the leading axis: part_o [S, ..., dim], part_lse [S, ...]."""
-    _need(part_o, "part_o", torch.float32)
+    """kv4_merge_states (fp32 part_o) or kv4_merge_states_f16 (fp16 part_o) over the leading axis:
+    part_o [S, ..., dim], part_lse [S, ...]."""
+    f16 = part_o.dtype == torch.float16
+    _need(part_o, "part_o", torch.float16 if f16 else torch.float32)
     _need(part_lse, "part_lse", torch.float32, part_o.device)
     if not part_o.is_contiguous() or not part_lse.is_contiguous() or part_o.shape[:-1] != part_lse.shape:
         raise ValueError("part_o [S, ..., dim] and part_lse [S, ...] must be contiguous and agree")
@@ -352,8 +359,9 @@ def merge_states(part_o, part_lse, out=None, lse=None, stream=None):
     _need(lse, "lse", torch.float32, part_o.device)
     if not out.is_contiguous() or out.numel() != n_states * dim or not lse.is_contiguous() or lse.numel() != n_states:
         raise ValueError("out / lse must be contiguous and match the parts")
-    _check(load().kv4_merge_states(_ptr(part_o), _ptr(part_lse), S, n_states, dim, _ptr(out), dim, _ptr(lse),
-                                   _stream(stream, part_o.device)))
+    fn = load().kv4_merge_states_f16 if f16 else load().kv4_merge_states
+    _check(fn(_ptr(part_o), _ptr(part_lse), S, n_states, dim, _ptr(out), dim, _ptr(lse),
+              _stream(stream, part_o.device)))
     return out, lse
 
 

@@ -153,6 +153,57 @@ kv4_status check_splits(const kv4_attn_args *a, int32_t num_splits, int32_t *out
     return ok();
 }
 
+// kv4_sparse_mla_decode_partial and its fp16 form: exactly one of o32, o16 is set
+kv4_status decode_partial(const kv4_attn_args *a, int32_t num_splits, float *o32, _Float16 *o16, float *part_lse,
+                          void *stream) {
+    kv4_status st = check_attn(a, false);
+    if (st != KV4_OK) return st;
+    if (num_splits < 1 || num_splits > KV4_MAX_SPLITS)
+        return fail(KV4_ERR_SHAPE, "num_splits = %d; need 1..%d", num_splits, KV4_MAX_SPLITS);
+    if (a->n_rows == 0) return ok();
+    if ((!o32 && !o16) || !part_lse) return fail(KV4_ERR_NULL, "part_o or part_lse is NULL");
+    if (o32 ? !aligned(o32, 16) : !aligned(o16, 8))
+        return fail(KV4_ERR_ALIGN, "part_o must be %d-byte aligned", o32 ? 16 : 8);
+    kv4::AttnParams p = base_params(a);
+    p.tiles_per_split = (n_tiles(a) + num_splits - 1) / num_splits;
+    p.out = o32;
+    p.out_h = o16;
+    p.out_row_stride = (int64_t)a->n_heads * KV4_LATENT;
+    p.out_split_stride = (int64_t)a->n_rows * a->n_heads * KV4_LATENT;
+    p.lse = part_lse;
+    p.lse_row_stride = a->n_heads;
+    p.lse_split_stride = (int64_t)a->n_rows * a->n_heads;
+    return hip_status(kv4::launch_sparse_mla(p, a->q_dtype == KV4_F32, num_splits, (hipStream_t)stream),
+                      "sparse_mla launch");
+}
+
+// kv4_merge_states and its fp16 form: exactly one of o32, o16 is set
+kv4_status merge_states(const float *o32, const _Float16 *o16, const float *part_lse, int32_t n_parts,
+                        int64_t n_states, int32_t dim, float *out, int64_t out_state_stride, float *lse, void *stream) {
+    if (n_parts < 1 || n_parts > 64) return fail(KV4_ERR_SHAPE, "n_parts = %d; need 1..64", n_parts);
+    if (n_states < 0 || n_states > 0x7FFFFFFF) return fail(KV4_ERR_SHAPE, "n_states out of range");
+    if (dim < 4 || dim > 4096 || dim % 4) return fail(KV4_ERR_SHAPE, "dim = %d; need a multiple of 4 in [4, 4096]", dim);
+    if (n_states == 0) return ok();
+    if ((!o32 && !o16) || !part_lse || !out) return fail(KV4_ERR_NULL, "part_o, part_lse or out is NULL");
+    if ((o32 ? !aligned(o32, 16) : !aligned(o16, 8)) || !aligned(out, 16))
+        return fail(KV4_ERR_ALIGN, "part_o must be %d-byte and out 16-byte aligned", o32 ? 16 : 8);
+    if (out_state_stride < dim || out_state_stride % 4)
+        return fail(KV4_ERR_ALIGN, "out_state_stride = %lld; need >= dim and a multiple of 4", (long long)out_state_stride);
+    kv4::MergeParams m{};
+    m.part_o = o32;
+    m.part_o_h = o16;
+    m.part_lse = part_lse;
+    m.n_parts = n_parts;
+    m.n_states = n_states;
+    m.dim = dim;
+    m.states_per_row = 1;
+    m.out = out;
+    m.out_row_stride = out_state_stride;
+    m.out_col_stride = 0;
+    m.lse = lse;
+    return hip_status(kv4::launch_merge_states(m, (hipStream_t)stream), "merge_states launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,29 +342,19 @@ size_t kv4_sparse_mla_decode_workspace(const kv4_attn_args *a, int32_t num_split
     if (check_attn(a, false) != KV4_OK) return 0;
     int32_t s = 0;
     if (check_splits(a, num_splits, &s) != KV4_OK || s <= 1) return 0;
+    // the splits' o as fp16 (256-byte padded), then their lse as fp32
     const size_t states = (size_t)s * a->n_rows * a->n_heads;
-    return states * KV4_LATENT * 4 + ((states * 4 + 255) / 256) * 256;
+    return ((states * KV4_LATENT * 2 + 255) / 256) * 256 + ((states * 4 + 255) / 256) * 256;
 }
 
 kv4_status kv4_sparse_mla_decode_partial(const kv4_attn_args *a, int32_t num_splits, float *part_o, float *part_lse,
                                          void *stream) {
-    kv4_status st = check_attn(a, false);
-    if (st != KV4_OK) return st;
-    if (num_splits < 1 || num_splits > KV4_MAX_SPLITS)
-        return fail(KV4_ERR_SHAPE, "num_splits = %d; need 1..%d", num_splits, KV4_MAX_SPLITS);
-    if (a->n_rows == 0) return ok();
-    if (!part_o || !part_lse) return fail(KV4_ERR_NULL, "part_o or part_lse is NULL");
-    if (!aligned(part_o, 16)) return fail(KV4_ERR_ALIGN, "part_o must be 16-byte aligned");
-    kv4::AttnParams p = base_params(a);
-    p.tiles_per_split = (n_tiles(a) + num_splits - 1) / num_splits;
-    p.out = part_o;
-    p.out_row_stride = (int64_t)a->n_heads * KV4_LATENT;
-    p.out_split_stride = (int64_t)a->n_rows * a->n_heads * KV4_LATENT;
-    p.lse = part_lse;
-    p.lse_row_stride = a->n_heads;
-    p.lse_split_stride = (int64_t)a->n_rows * a->n_heads;
-    return hip_status(kv4::launch_sparse_mla(p, a->q_dtype == KV4_F32, num_splits, (hipStream_t)stream),
-                      "sparse_mla launch");
+    return decode_partial(a, num_splits, part_o, nullptr, part_lse, stream);
+}
+
+kv4_status kv4_sparse_mla_decode_partial_f16(const kv4_attn_args *a, int32_t num_splits, void *part_o,
+                                             float *part_lse, void *stream) {
+    return decode_partial(a, num_splits, nullptr, static_cast<_Float16 *>(part_o), part_lse, stream);
 }
 
 kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, void *workspace, size_t workspace_bytes,
@@ -340,11 +381,16 @@ kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, voi
         return fail(KV4_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed for %d splits", workspace ? workspace_bytes : 0,
                     need, s);
     if (!aligned(workspace, 256)) return fail(KV4_ERR_ALIGN, "workspace must be 256-byte aligned");
+    // The splits' o travel as fp16: each is a convex combination of latent
+    // values, so |o| <= 6 * 448 = 2688 (within fp16's range) and the rounding
+    // adds at most 2^-11 of |o| relative to the fp32 state.
     const size_t states = (size_t)s * a->n_rows * a->n_heads;
-    float *part_o = static_cast<float *>(workspace);
-    float *part_lse = part_o + states * KV4_LATENT;
+    _Float16 *part_o = static_cast<_Float16 *>(workspace);
+    float *part_lse = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                                ((states * KV4_LATENT * 2 + 255) / 256) * 256);
     p.tiles_per_split = (n_tiles(a) + s - 1) / s;
-    p.out = part_o;
+    p.out = nullptr;
+    p.out_h = part_o;
     p.out_row_stride = (int64_t)a->n_heads * KV4_LATENT;
     p.out_split_stride = (int64_t)a->n_rows * a->n_heads * KV4_LATENT;
     p.lse = part_lse;
@@ -353,7 +399,7 @@ kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, voi
     st = hip_status(kv4::launch_sparse_mla(p, a->q_dtype == KV4_F32, s, (hipStream_t)stream), "sparse_mla launch");
     if (st != KV4_OK) return st;
     kv4::MergeParams m{};
-    m.part_o = part_o;
+    m.part_o_h = part_o;
     m.part_lse = part_lse;
     m.n_parts = s;
     m.n_states = (int64_t)a->n_rows * a->n_heads;
@@ -368,26 +414,13 @@ kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, voi
 
 kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t n_parts, int64_t n_states, int32_t dim,
                             float *out, int64_t out_state_stride, float *lse, void *stream) {
-    if (n_parts < 1 || n_parts > 64) return fail(KV4_ERR_SHAPE, "n_parts = %d; need 1..64", n_parts);
-    if (n_states < 0 || n_states > 0x7FFFFFFF) return fail(KV4_ERR_SHAPE, "n_states out of range");
-    if (dim < 4 || dim > 4096 || dim % 4) return fail(KV4_ERR_SHAPE, "dim = %d; need a multiple of 4 in [4, 4096]", dim);
-    if (n_states == 0) return ok();
-    if (!part_o || !part_lse || !out) return fail(KV4_ERR_NULL, "part_o, part_lse or out is NULL");
-    if (!aligned(part_o, 16) || !aligned(out, 16)) return fail(KV4_ERR_ALIGN, "part_o and out must be 16-byte aligned");
-    if (out_state_stride < dim || out_state_stride % 4)
-        return fail(KV4_ERR_ALIGN, "out_state_stride = %lld; need >= dim and a multiple of 4", (long long)out_state_stride);
-    kv4::MergeParams m{};
-    m.part_o = part_o;
-    m.part_lse = part_lse;
-    m.n_parts = n_parts;
-    m.n_states = n_states;
-    m.dim = dim;
-    m.states_per_row = 1;
-    m.out = out;
-    m.out_row_stride = out_state_stride;
-    m.out_col_stride = 0;
-    m.lse = lse;
-    return hip_status(kv4::launch_merge_states(m, (hipStream_t)stream), "merge_states launch");
+    return merge_states(part_o, nullptr, part_lse, n_parts, n_states, dim, out, out_state_stride, lse, stream);
+}
+
+kv4_status kv4_merge_states_f16(const void *part_o, const float *part_lse, int32_t n_parts, int64_t n_states,
+                                int32_t dim, float *out, int64_t out_state_stride, float *lse, void *stream) {
+    return merge_states(nullptr, static_cast<const _Float16 *>(part_o), part_lse, n_parts, n_states, dim, out,
+                        out_state_stride, lse, stream);
 }
 
 size_t kv4_global_compact_workspace(const kv4_attn_args *a) {

@@ -25,6 +25,7 @@ struct AttnParams {
     int32_t tiles_per_split;   // tiles of 32 entries per split
     float score_mul;           // sm_scale * log2(e)
     float *out;                // element (s, r, h, d) at s*out_split_stride + r*out_row_stride + h*512 + d
+    _Float16 *out_h;           // non-null: o goes here instead, as fp16, at the same element offsets
     int64_t out_row_stride, out_split_stride;
     float *lse;                // element (s, r, h) at s*lse_split_stride + r*lse_row_stride + h
     int64_t lse_row_stride, lse_split_stride;
@@ -40,6 +41,7 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 
 struct MergeParams {
     const float *part_o;       // (s, t, d) at (s * n_states + t) * dim + d
+    const _Float16 *part_o_h;  // non-null: the parts' o as fp16 (same offsets), part_o unused
     const float *part_lse;     // (s, t) at s * n_states + t
     int32_t n_parts;
     int64_t n_states;

@@ -64,6 +64,7 @@ constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 // K-tile layout, chunk-major: element (row r, dim d) is at
 // (d / 8) * 576 + 16 r + 2 (d % 8), i.e. the 32 rows' copies of one 16-byte
@@ -689,11 +690,22 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     __syncthreads();
     {
         const uint32_t orr = pin(oreg + 16 * lane);
-        float *ob = p.out + (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + 256 * half + 4 * lane;
+        const int64_t ob = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + 256 * half + 4 * lane;
+        if (p.out_h) {                             // fp16 split partials (|o| <= 2688): half the bytes to store
 #pragma unroll
-        for (int h = 0; h < 32; ++h) {
-            const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
-            if (hg * 32 + h < p.n_heads) *reinterpret_cast<floatx4_t *>(ob + (int64_t)(hg * 32 + h) * kLatent) = v;
+            for (int h = 0; h < 32; ++h) {
+                const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
+                if (hg * 32 + h < p.n_heads)
+                    *reinterpret_cast<half4_t *>(p.out_h + ob + (int64_t)(hg * 32 + h) * kLatent) =
+                        __builtin_convertvector(v, half4_t);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 32; ++h) {
+                const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
+                if (hg * 32 + h < p.n_heads)
+                    *reinterpret_cast<floatx4_t *>(p.out + ob + (int64_t)(hg * 32 + h) * kLatent) = v;
+            }
         }
     }
     if (head_live && half == 0 && g == 0 && p.lse) {
@@ -795,20 +807,28 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 // order) / W, lse = M + ln W; all parts empty gives o = 0, lse = -inf.
 constexpr int kMergeBatch = 8;
 
+// four consecutive dims of one part's o, widened to fp32 (exact) from fp16 parts
+template <bool F16>
+__device__ __forceinline__ floatx4_t load_part4(const MergeParams &p, int64_t off) {
+    if constexpr (F16) return __builtin_convertvector(*reinterpret_cast<const half4_t *>(p.part_o_h + off), floatx4_t);
+    else return *reinterpret_cast<const floatx4_t *>(p.part_o + off);
+}
+
+template <bool F16>
 __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
     __shared__ float w[64];
     __shared__ float stat[2];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int S = p.n_parts;
-    const float *o_t = p.part_o + t * p.dim;                      // part s at s * n_states * dim
+    const int64_t o_t = t * p.dim;                                // part s at s * n_states * dim
     const int64_t o_stride = p.n_states * (int64_t)p.dim;
     const bool early = S <= kMergeBatch && p.dim <= 512;          // uniform
     floatx4_t v[kMergeBatch];
     if (early && 4 * tid < p.dim) {
 #pragma unroll
         for (int s = 0; s < kMergeBatch; ++s)
-            if (s < S) v[s] = *reinterpret_cast<const floatx4_t *>(o_t + s * o_stride + 4 * tid);
+            if (s < S) v[s] = load_part4<F16>(p, o_t + s * o_stride + 4 * tid);
     }
     if (tid == 0) {
         float M = -__builtin_inff();
@@ -854,7 +874,7 @@ __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
         if (W > 0.0f)
             for (int s = 0; s < S; ++s) {
                 const float ws = w[s];
-                if (ws != 0.0f) acc += ws * *reinterpret_cast<const floatx4_t *>(o_t + s * o_stride + d);
+                if (ws != 0.0f) acc += ws * load_part4<F16>(p, o_t + s * o_stride + d);
             }
         *reinterpret_cast<floatx4_t *>(orow + d) = acc * inv;
     }
@@ -862,7 +882,8 @@ __global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
 
 hipError_t launch_merge_states(const MergeParams &p, hipStream_t stream) {
     if (p.n_states == 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)p.n_states), dim3(128), 0, stream, p);
+    if (p.part_o_h) hipLaunchKernelGGL(merge_states_kernel<true>, dim3((unsigned)p.n_states), dim3(128), 0, stream, p);
+    else hipLaunchKernelGGL(merge_states_kernel<false>, dim3((unsigned)p.n_states), dim3(128), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -229,7 +229,11 @@ size_t kv4_sparse_mla_decode_workspace(const kv4_attn_args *a, int32_t num_split
  * instead of into an FP8 scratch copy).  Splits each row's list into
  * num_splits contiguous parts (0 = automatic, 1..KV4_MAX_SPLITS), computes a
  * normalised (o, lse) per part from 4-bit rows dequantized on chip, and merges
- * the parts into out/lse.
+ * the parts into out/lse.  The parts' o are held in the workspace as fp16
+ * (round to nearest even; a part's o is a convex combination of latent values,
+ * so |o| <= 2688 and the rounding error is at most 2^-11 of |o|), their lse as
+ * fp32: the result equals kv4_merge_states over kv4_sparse_mla_decode_partial's
+ * parts with each o first rounded to fp16.
  *   workspace     device, >= kv4_sparse_mla_decode_workspace(a, num_splits)
  *                 bytes, 256-byte aligned; may be NULL when that is 0.
  *                 Its contents are scratch; two calls in flight must not share it.
@@ -253,6 +257,17 @@ kv4_status kv4_sparse_mla_decode_partial(const kv4_attn_args *a, int32_t num_spl
                                          float *part_lse, void *stream);
 
 /*
+ * kv4_sparse_mla_decode_partial with the parts' o written as fp16 (round to
+ * nearest even; |o| <= 2688, so the rounding error is at most 2^-11 of |o|):
+ * the form kv4_sparse_mla_decode keeps in its workspace, which halves the
+ * bytes the parts cost to write and to merge.
+ *   part_o        device fp16 bit patterns at the offsets above, 8-byte aligned.
+ * Errors as kv4_sparse_mla_decode.
+ */
+kv4_status kv4_sparse_mla_decode_partial_f16(const kv4_attn_args *a, int32_t num_splits, void *part_o,
+                                             float *part_lse, void *stream);
+
+/*
  * Merge of attention states (README, "Parallelism and disaggregation": each
  * rank returns (o, lse) to a merge).  For each state t in [0, n_states):
  *   M = max_s lse_s, w_s = exp(lse_s - M), W = sum_s w_s
@@ -268,6 +283,15 @@ kv4_status kv4_sparse_mla_decode_partial(const kv4_attn_args *a, int32_t num_spl
 kv4_status kv4_merge_states(const float *part_o, const float *part_lse, int32_t n_parts,
                             int64_t n_states, int32_t dim, float *out, int64_t out_state_stride,
                             float *lse, void *stream);
+
+/*
+ * kv4_merge_states over parts whose o are fp16 bit patterns (as
+ * kv4_sparse_mla_decode_partial_f16 writes them), 8-byte aligned; each is
+ * widened exactly to fp32 and merged as above.  Errors as kv4_merge_states.
+ */
+kv4_status kv4_merge_states_f16(const void *part_o, const float *part_lse, int32_t n_parts,
+                                int64_t n_states, int32_t dim, float *out, int64_t out_state_stride,
+                                float *lse, void *stream);
 
 /*
  * Dequantizing gather (README, "4-bit KV cache": the dequantizing gather).

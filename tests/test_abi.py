@@ -107,12 +107,33 @@ def test_decode_split_and_workspace_checks():
     # 2 splits need a workspace; none given
     assert lib.kv4_sparse_mla_decode(ctypes.byref(a), 2, None, 0, None) == 5
     need = lib.kv4_sparse_mla_decode_workspace(ctypes.byref(a), 2)
-    assert need == 2 * 2 * 64 * 512 * 4 + 2 * 2 * 64 * 4
+    assert need == 2 * 2 * 64 * 512 * 2 + 2 * 2 * 64 * 4   # fp16 o of each part, fp32 lse
     assert lib.kv4_sparse_mla_decode(ctypes.byref(a), 2, ctypes.c_void_p(0x100000), need - 1, None) == 5
     assert lib.kv4_sparse_mla_decode(ctypes.byref(a), 2, ctypes.c_void_p(0x100010), need, None) == 3
     assert lib.kv4_sparse_mla_decode_workspace(ctypes.byref(a), 1) == 0
     assert lib.kv4_sparse_mla_decode_partial(ctypes.byref(a), 0, None, None, None) == 2
     assert lib.kv4_sparse_mla_decode_partial(ctypes.byref(a), 2, None, None, None) == 1
+    # fp16 parts: the same checks, 8-byte alignment of part_o
+    V = ctypes.c_void_p
+    assert lib.kv4_sparse_mla_decode_partial_f16(ctypes.byref(a), 0, None, None, None) == 2
+    assert lib.kv4_sparse_mla_decode_partial_f16(ctypes.byref(a), 2, None, V(0x100000), None) == 1
+    assert lib.kv4_sparse_mla_decode_partial_f16(ctypes.byref(a), 2, V(0x100004), V(0x200000), None) == 3
+    assert lib.kv4_sparse_mla_decode_partial(ctypes.byref(a), 2, V(0x100008), V(0x200000), None) == 3
+
+
+def test_merge_states_argument_checks():
+    lib = kv4.load()
+    V = ctypes.c_void_p
+    for f, bad_align in ((lib.kv4_merge_states, 0x1008), (lib.kv4_merge_states_f16, 0x1004)):
+        assert f(V(0x1000), V(0x2000), 0, 4, 512, V(0x3000), 512, None, None) == 2     # n_parts
+        assert f(V(0x1000), V(0x2000), 65, 4, 512, V(0x3000), 512, None, None) == 2
+        assert f(V(0x1000), V(0x2000), 2, 4, 510, V(0x3000), 512, None, None) == 2     # dim % 4
+        assert f(V(0x1000), V(0x2000), 2, 0, 512, V(0x3000), 512, None, None) == 0     # nothing to do
+        assert f(None, V(0x2000), 2, 4, 512, V(0x3000), 512, None, None) == 1
+        assert f(V(0x1000), V(0x2000), 2, 4, 512, None, 512, None, None) == 1
+        assert f(V(bad_align), V(0x2000), 2, 4, 512, V(0x3000), 512, None, None) == 3
+        assert f(V(0x1000), V(0x2000), 2, 4, 512, V(0x3008), 512, None, None) == 3
+        assert f(V(0x1000), V(0x2000), 2, 4, 512, V(0x3000), 508, None, None) == 3     # stride < dim
 
 
 def test_zero_rows_is_a_no_op():

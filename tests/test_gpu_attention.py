@@ -74,8 +74,9 @@ def test_c5_prefill_rows_subset():
 
 # ----------------------------------------------------- equalities of paths
 def test_partial_plus_merge_equals_decode_bitwise():
-    """Decode equals its two exposed halves bit for bit, for several split
-    counts (16 and 17 included) run on one workspace, some twice in a row."""
+    """Decode equals its two exposed halves bit for bit once the parts' o are
+    rounded to fp16 (the workspace holds them so), for several split counts
+    (16 and 17 included) run on one workspace, some twice in a row."""
     spec = W.C2
     pool_d, _ = pools(spec)
     q, topk, pt = to_dev(W.queries(spec)), to_dev(W.topk_lists(spec)), to_dev(W.page_table(spec))
@@ -85,9 +86,15 @@ def test_partial_plus_merge_equals_decode_bitwise():
     for s in splits:
         out, lse = kv4.sparse_mla_decode(q, pool_d, topk, spec.sm_scale, page_table=pt, num_splits=s, workspace=ws)
         po, pl = kv4.sparse_mla_decode_partial(q, pool_d, topk, spec.sm_scale, s, page_table=pt)
-        o2, l2 = kv4.merge_states(po, pl)
+        ph, plh = kv4.sparse_mla_decode_partial(q, pool_d, topk, spec.sm_scale, s, page_table=pt,
+                                                parts_dtype=torch.float16)
+        o2, l2 = kv4.merge_states(po.half().float(), pl)
+        o3, l3 = kv4.merge_states(ph, plh)
         torch.cuda.synchronize()
+        # the fp16 parts are the fp32 parts rounded to nearest even (torch's rounding)
+        assert torch.equal(ph, po.half()) and torch.equal(plh, pl), "splits=%d" % s
         assert torch.equal(out, o2) and torch.equal(lse, l2), "splits=%d" % s
+        assert torch.equal(out, o3) and torch.equal(lse, l3), "splits=%d" % s
 
 
 def test_prefill_equals_single_split_decode_bitwise():

@@ -21,7 +21,9 @@ def test_c3_long_context_decode_sampled():
     st, pool, pt = wl["sets"][0], wl["pool"], wl["pt"]
     S = kv4.sparse_mla_decode_splits(st["q"], pool, st["topk"], page_table=pt)
     lists, counts = kv4.dedup_compact(st["topk"])
-    po, pl = kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt)
+    # the launch configuration the benchmark times: fp16 parts, then their merge
+    po, pl = kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt,
+                                           parts_dtype=torch.float16)
     out, lse = kv4.merge_states(po, pl)
     torch.cuda.synchronize()
     assert (counts.cpu().numpy() == spec.k).all()
