@@ -259,15 +259,22 @@ def main():
     per_step_ms = (time.perf_counter() - t2) / args.steps * 1e3
 
     # Average launch duration of the split kernel (and of the merge): a graph
-    # of LAUNCHES back-to-back launches replayed REPS times between events on
-    # the stream they run on.
-    LAUNCHES, REPS = 10, 5
+    # of LAUNCHES back-to-back launches, launch i on rotating input set i % 8,
+    # replayed REPS times between events on the stream they run on.  The
+    # workload's lists hold no repeats, so a set's raw lists are its
+    # compacted ones.
+    LAUNCHES, REPS = 16, 5
+    for i in range(n_sets):
+        step(i)
+        torch.cuda.synchronize(dev)
+        if not bool((counts == K).all()):
+            raise RuntimeError("input set %d: a list holds repeats, so its raw and compacted lists differ" % i)
 
     def launch_ms(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(LAUNCHES):
-                fn()
+            for i in range(LAUNCHES):
+                fn(i % n_sets)
         g.replay()
         torch.cuda.synchronize(dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -278,14 +285,14 @@ def main():
         torch.cuda.synchronize(dev)
         return e0.elapsed_time(e1) / (LAUNCHES * REPS)
 
-    st0 = sets[0]
     if S > 1:
-        split_ms = launch_ms(lambda: kv4.sparse_mla_decode_partial(st0["q"], pool, lists, spec.sm_scale, S, page_table=pt,
-                                                                   part_o=part_o, part_lse=part_lse))
-        merge_ms = launch_ms(lambda: kv4.merge_states(part_o, part_lse, out=out, lse=lse))
+        split_ms = launch_ms(lambda i: kv4.sparse_mla_decode_partial(sets[i]["q"], pool, sets[i]["topk"], spec.sm_scale,
+                                                                     S, page_table=pt, part_o=part_o,
+                                                                     part_lse=part_lse))
+        merge_ms = launch_ms(lambda i: kv4.merge_states(part_o, part_lse, out=out, lse=lse))
     else:
-        split_ms = launch_ms(lambda: kv4.sparse_mla_decode(st0["q"], pool, lists, spec.sm_scale, page_table=pt,
-                                                           num_splits=1, out=out, lse=lse))
+        split_ms = launch_ms(lambda i: kv4.sparse_mla_decode(sets[i]["q"], pool, sets[i]["topk"], spec.sm_scale,
+                                                             page_table=pt, num_splits=1, out=out, lse=lse))
         merge_ms = 0.0
 
     if args.calib_copy:
@@ -359,16 +366,16 @@ def run_rope_free(spec, wl, dev, S, launch_ms):
         lo = c * W.KV_CHUNK
         kv4.quant_write(x, torch.arange(lo, lo + x.shape[0], dtype=torch.int32, device=dev), pool)
         del x
-    st = wl["sets"][0]
-    q = st["q"][:, :, :512].contiguous()
+    sets = wl["sets"]
+    qs = [st["q"][:, :, :512].contiguous() for st in sets]
     scale = 1.0 / np.sqrt(512.0)
     R, H, K = spec.n_req, spec.n_heads, spec.k
-    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(q, pool, st["topk"], S, page_table=wl["pt"])),
+    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(qs[0], pool, sets[0]["topk"], S, page_table=wl["pt"])),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((R, H), dtype=torch.float32, device=dev)
-    ms = launch_ms(lambda: kv4.sparse_mla_decode(q, pool, st["topk"], scale, page_table=wl["pt"], num_splits=S,
-                                                 workspace=ws, out=out, lse=lse))
+    ms = launch_ms(lambda i: kv4.sparse_mla_decode(qs[i], pool, sets[i]["topk"], scale, page_table=wl["pt"],
+                                                   num_splits=S, workspace=ws, out=out, lse=lse))
     algo = algorithmic_decode_bytes(R, H, K, row_bytes=kv4.ROW_BYTES_ROPE_FREE, dim=512)
     del pool
     torch.cuda.empty_cache()
