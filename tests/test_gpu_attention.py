@@ -97,6 +97,28 @@ def test_partial_plus_merge_equals_decode_bitwise():
         assert torch.equal(out, o3) and torch.equal(lse, l3), "splits=%d" % s
 
 
+def test_fp16_parts_stay_within_their_rounding_bound():
+    """Decode with fp16 parts differs from the merge of the fp32 parts by at
+    most the fp16 rounding of the largest part, elementwise: the merged o is a
+    convex combination of the parts, and rounding to nearest even moves each
+    part's o by at most 2^-11 |o_s| (fp16's unit roundoff; |o_s| <= 2688) or,
+    in fp16's subnormal range, 2^-25; the two merges' own fp32 roundings add
+    a few fp32 ulp of the largest part."""
+    spec = W.C2
+    pool_d, _ = pools(spec)
+    q, topk, pt = to_dev(W.queries(spec)), to_dev(W.topk_lists(spec)), to_dev(W.page_table(spec))
+    for s in (2, 4, 8):
+        o16, _ = kv4.sparse_mla_decode(q, pool_d, topk, spec.sm_scale, page_table=pt, num_splits=s)
+        po, pl = kv4.sparse_mla_decode_partial(q, pool_d, topk, spec.sm_scale, s, page_table=pt)
+        o32, _ = kv4.merge_states(po, pl)
+        torch.cuda.synchronize()
+        part_max = po.abs().amax(dim=0).double()                        # max_s |o_s| per element
+        bound = 2.0 ** -11 * part_max + 2.0 ** -25 + 16 * 2.0 ** -24 * part_max
+        diff = (o16.double() - o32.double()).abs()
+        assert (diff <= bound).all(), "splits=%d: worst excess %.3g" % (s, float((diff - bound).max()))
+        assert float(diff.max()) > 0.0          # the fp16 parts are in use
+
+
 def test_prefill_equals_single_split_decode_bitwise():
     spec = W.scaled(W.C5, n_query_rows=16, first_query_pos=W.C5.ctx - 16)
     pool_d, _ = pools(spec)
