@@ -65,6 +65,7 @@ def _args():
     ap.add_argument("--no-write", action="store_true", help="skip the write + compaction measurement")
     ap.add_argument("--no-rope-free", action="store_true", help="skip the rope-free (288-byte row) decode measurement")
     ap.add_argument("--no-compact", action="store_true", help="skip the global compaction measurements")
+    ap.add_argument("--no-c2", action="store_true", help="skip the batch-8 decode (one GPU's head share) measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size kernel for counter calibration)")
@@ -357,6 +358,8 @@ def main():
     result["roofline"]["frac_of_measured_copy"] = round(achieved / result["measured_ceilings"]["copy_gbs"], 4)
     if not args.no_rope_free:
         result["rope_free_decode"] = run_rope_free(spec, wl, dev, S, launch_ms)
+    if not args.no_c2 and args.workload == "c3":
+        result["c2_decode"] = run_c2_decode(dev)
     if not args.no_compact:
         print("[bench] global compaction of the decode lists", file=sys.stderr, flush=True)
         result["global_compact_decode"] = run_global_compact(spec.name + " lists", pool, sets[0]["topk"], pt, None,
@@ -404,6 +407,60 @@ def run_rope_free(spec, wl, dev, S, launch_ms):
             "splits": S, "decode_ms": round(ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
             "algorithmic_bytes": algo, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "note": "one decode call (split kernel and merge) per token batch; the step's write and dedup not included"}
+
+
+def run_c2_decode(dev, n_pools=6):
+    """Config C2, one GPU's 64-head share at batch 8: the decode call
+    (automatic split count: the split kernel and the merge) over n_pools
+    independent pools with their own page tables, lists and queries (6 x 92 MB,
+    so the gathered rows do not sit in the 256 MB MALL); average of a HIP graph
+    of 12 calls cycling through them, replayed 5 times between events."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+    spec = W.C2
+    print("[bench] decode %s" % spec.name, file=sys.stderr, flush=True)
+    wls = [build_decode_workload(W.scaled(spec, seed=spec.seed + 101 * i), dev, n_sets=1) for i in range(n_pools)]
+    R, H, K = spec.n_req, spec.n_heads, spec.k
+    S = kv4.sparse_mla_decode_splits(wls[0]["sets"][0]["q"], wls[0]["pool"], wls[0]["sets"][0]["topk"],
+                                     page_table=wls[0]["pt"])
+    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(wls[0]["sets"][0]["q"], wls[0]["pool"],
+                                                            wls[0]["sets"][0]["topk"], S, page_table=wls[0]["pt"])),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    CALLS, REPS = 12, 5
+
+    def call(i):
+        w = wls[i % n_pools]
+        kv4.sparse_mla_decode(w["sets"][0]["q"], w["pool"], w["sets"][0]["topk"], spec.sm_scale, page_table=w["pt"],
+                              num_splits=S, workspace=ws, out=out, lse=lse)
+
+    call(0)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(CALLS):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize(dev)
+    warm(g.replay, dev, SECTION_WARM_S[0])
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(REPS):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / (CALLS * REPS)
+    algo = algorithmic_decode_bytes(R, H, K)
+    gbs = algo / (ms * 1e-3) / 1e9
+    del wls
+    torch.cuda.empty_cache()
+    return {"workload": spec.name, "requests": R, "heads": H, "topk": K, "context_tokens": spec.ctx, "splits": S,
+            "pools": n_pools, "decode_us": round(ms * 1e3, 2), "tokens_per_s": round(R / (ms * 1e-3), 1),
+            "algorithmic_bytes": algo, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "one decode call (split kernel and merge) per token batch of 8"}
 
 
 def measure_ceilings(dev):
