@@ -65,7 +65,8 @@ def _args():
     ap.add_argument("--no-write", action="store_true", help="skip the write + compaction measurement")
     ap.add_argument("--no-rope-free", action="store_true", help="skip the rope-free (288-byte row) decode measurement")
     ap.add_argument("--no-compact", action="store_true", help="skip the global compaction measurements")
-    ap.add_argument("--no-c2", action="store_true", help="skip the batch-8 decode (one GPU's head share) measurement")
+    ap.add_argument("--no-c2", action="store_true",
+                    help="skip the tiny (batch 1) and batch-8 (one GPU's head share) decode measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (a known-size kernel for counter calibration)")
@@ -359,6 +360,7 @@ def main():
     if not args.no_rope_free:
         result["rope_free_decode"] = run_rope_free(spec, wl, dev, S, launch_ms)
     if not args.no_c2 and args.workload == "c3":
+        result["c1_decode"] = run_c1_decode(dev)
         result["c2_decode"] = run_c2_decode(dev)
     if not args.no_compact:
         print("[bench] global compaction of the decode lists", file=sys.stderr, flush=True)
@@ -407,6 +409,52 @@ def run_rope_free(spec, wl, dev, S, launch_ms):
             "splits": S, "decode_ms": round(ms, 5), "tokens_per_s": round(R / (ms * 1e-3), 1),
             "algorithmic_bytes": algo, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "note": "one decode call (split kernel and merge) per token batch; the step's write and dedup not included"}
+
+
+def run_c1_decode(dev):
+    """Config C1, tiny decode (1 request, 16 heads, fp32 queries, top-256 of a
+    4096-token context): latency of one decode call (automatic split count:
+    the split kernel and the merge), from a HIP graph of 20 calls replayed 5
+    times between events; tokens/s = 1 / t."""
+    import torch
+    import bit_kv_cache_kv4_amd as kv4
+    import workloads as W
+    spec = W.C1
+    print("[bench] decode %s" % spec.name, file=sys.stderr, flush=True)
+    wl = build_decode_workload(spec, dev, n_sets=1)
+    st = wl["sets"][0]
+    S = kv4.sparse_mla_decode_splits(st["q"], wl["pool"], st["topk"], page_table=wl["pt"])
+    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(st["q"], wl["pool"], st["topk"], S, page_table=wl["pt"])),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((spec.n_req, spec.n_heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((spec.n_req, spec.n_heads), dtype=torch.float32, device=dev)
+    CALLS, REPS = 20, 5
+
+    def call():
+        kv4.sparse_mla_decode(st["q"], wl["pool"], st["topk"], spec.sm_scale, page_table=wl["pt"], num_splits=S,
+                              workspace=ws, out=out, lse=lse)
+
+    call()
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(CALLS):
+            call()
+    g.replay()
+    torch.cuda.synchronize(dev)
+    warm(g.replay, dev, SECTION_WARM_S[0])
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(REPS):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / (CALLS * REPS)
+    return {"workload": spec.name, "requests": spec.n_req, "heads": spec.n_heads, "topk": spec.k,
+            "context_tokens": spec.ctx, "q_dtype": spec.q_dtype, "splits": S, "decode_us": round(ms * 1e3, 2),
+            "tokens_per_s": round(spec.n_req / (ms * 1e-3), 1),
+            "note": "launch-latency bound: 0.16 MB and 8.9 MFLOP per call"}
 
 
 def run_c2_decode(dev, n_pools=6):
