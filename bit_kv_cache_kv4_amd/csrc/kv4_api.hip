@@ -134,12 +134,17 @@ int32_t auto_splits(const kv4_attn_args *a) {
     // 32 entries per split: a split's fixed cost (list, page table, queries,
     // first gathers, the state written and merged) is worth a few tiles.
     // Measured on 8 rows x 64 heads x 2048 entries: 5 splits 46.4 us, 8 37.0,
-    // 16 33.5, 32 40.0; on 64 rows the compute units bound it at 4.
+    // 16 33.5, 32 40.0; on 64 rows the compute units bound it at 4.  When the
+    // merge has fewer states than compute units its cost hardly grows with the
+    // split count, and two tiles per split suffice (1 row x 16 heads x 256
+    // entries: 2 splits 23.2 us, 4 21.4, 8 22.2).
     const int32_t tiles = n_tiles(a);
     if (tiles <= 1 || a->n_rows == 0) return 1;
     const int64_t base = (int64_t)a->n_rows * ((a->n_heads + 63) / 64);
-    int64_t s = (device_cu_count() + base - 1) / base;
-    s = std::min<int64_t>(s, std::max<int32_t>(1, tiles / 4));
+    const int64_t cus = device_cu_count();
+    int64_t s = (cus + base - 1) / base;
+    const int32_t min_tiles = (int64_t)a->n_rows * a->n_heads < cus ? 2 : 4;
+    s = std::min<int64_t>(s, std::max<int32_t>(1, tiles / min_tiles));
     s = std::min<int64_t>(s, KV4_MAX_SPLITS);
     return (int32_t)std::max<int64_t>(s, 1);
 }
