@@ -154,7 +154,7 @@ def _check_write_args(kv, slots, pool, err_word, rope_free=False):
     if err_word is not None:
         _need(err_word, "err_word", torch.int32, kv.device)
     if kv.dim() != 2 or slots.dim() != 1 or slots.numel() != kv.shape[0] or (
-            kv.shape[0] > 0 and (kv.stride(1) != 1 or slots.stride(0) != 1)):
+            kv.shape[0] > 0 and (kv.stride(1) != 1 or (slots.shape[0] > 1 and slots.stride(0) != 1))):
         raise ValueError("kv must be [N, >=576] with unit inner stride and slots [N] contiguous")
     dim, row = (LATENT, ROW_BYTES_ROPE_FREE) if rope_free else (DIM, ROW_BYTES)
     if kv.shape[1] < dim:
@@ -168,11 +168,11 @@ def quant_write(kv, slots, pool, err_word=None, stream=None) -> None:
     rope-free pool ([n_slots, 288]) kv4_quant_write_rope_free of fp32 [N, >=512] rows."""
     if pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE:
         _check_write_args(kv, slots, pool, err_word, rope_free=True)
-        _check(load().kv4_quant_write_rope_free(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool),
+        _check(load().kv4_quant_write_rope_free(_ptr(kv), _stride(kv, 0), _ptr(slots), kv.shape[0], _ptr(pool),
                                                 pool.shape[0], _ptr(err_word), _stream(stream, kv.device)))
         return
     _check_write_args(kv, slots, pool, err_word)
-    _check(load().kv4_quant_write(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
+    _check(load().kv4_quant_write(_ptr(kv), _stride(kv, 0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
                                   _ptr(err_word), _stream(stream, kv.device)))
 
 
@@ -181,7 +181,7 @@ def quant_write_mse(kv, slots, pool, err_word=None, stream=None) -> None:
     (352-byte rows from 576 values, or 288-byte rope-free rows from 512) follows the pool."""
     rope_free = pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE
     _check_write_args(kv, slots, pool, err_word, rope_free=rope_free)
-    _check(load().kv4_quant_write_mse(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
+    _check(load().kv4_quant_write_mse(_ptr(kv), _stride(kv, 0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
                                       _ROW_ROPE_FREE if rope_free else _ROW_ROPE, _ptr(err_word),
                                       _stream(stream, kv.device)))
 
@@ -206,7 +206,7 @@ def _dedup_outputs(idx, k, out_idx, out_count):
 def dedup_compact(idx, k=None, out_idx=None, out_count=None, stream=None):
     """kv4_dedup_compact: per list, first occurrences of values >= 0 in order, -1 fill, counts."""
     n, k, out_idx, out_count = _dedup_outputs(idx, k, out_idx, out_count)
-    _check(load().kv4_dedup_compact(_ptr(idx), n, k, idx.stride(0), _ptr(out_idx), _ptr(out_count),
+    _check(load().kv4_dedup_compact(_ptr(idx), n, k, _stride(idx, 0), _ptr(out_idx), _ptr(out_count),
                                     _stream(stream, idx.device)))
     return out_idx, out_count
 
@@ -218,13 +218,25 @@ def write_and_dedup(kv, slots, pool, idx, k=None, out_idx=None, out_count=None, 
     if idx.device != kv.device:
         raise ValueError("idx must be on the device of kv")
     n, k, out_idx, out_count = _dedup_outputs(idx, k, out_idx, out_count)
-    _check(load().kv4_write_and_dedup(_ptr(kv), kv.stride(0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
-                                      _ptr(err_word), _ptr(idx), n, k, idx.stride(0), _ptr(out_idx),
+    _check(load().kv4_write_and_dedup(_ptr(kv), _stride(kv, 0), _ptr(slots), kv.shape[0], _ptr(pool), pool.shape[0],
+                                      _ptr(err_word), _ptr(idx), n, k, _stride(idx, 0), _ptr(out_idx),
                                       _ptr(out_count), _stream(stream, kv.device)))
     return out_idx, out_count
 
 
 # -------------------------------------------------------------- attention
+def _stride(t, d):
+    """Element stride of dimension d; a dimension of size 1 is never stepped
+    over, and its stride (which torch and numpy leave arbitrary, often 0) is
+    reported as the size of the dimensions inside it."""
+    if t.shape[d] == 1:
+        n = 1
+        for x in t.shape[d + 1:]:
+            n *= x
+        return n
+    return t.stride(d)
+
+
 def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse, err_word, k=None):
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q must be bfloat16 or float32")
@@ -246,7 +258,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
     a = AttnArgs()
     a.struct_size = ctypes.sizeof(AttnArgs)
     a.q_dtype = _BF16 if q.dtype == torch.bfloat16 else _F32
-    a.q, a.q_row_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
+    a.q, a.q_row_stride, a.q_head_stride = q.data_ptr(), _stride(q, 0), _stride(q, 1)
     a.n_rows, a.n_heads = q.shape[0], q.shape[1]
     a.pool, a.n_slots = pool.data_ptr(), pool.shape[0]
     a.row_format = _ROW_ROPE_FREE if rope_free else _ROW_ROPE
@@ -254,7 +266,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
         _need(page_table, "page_table", torch.int32, dev)
         if page_table.dim() != 2 or page_table.stride(1) != 1:
             raise ValueError("page_table must be [n_req, n_pages] with unit inner stride")
-        a.page_table, a.pt_row_stride = page_table.data_ptr(), page_table.stride(0)
+        a.page_table, a.pt_row_stride = page_table.data_ptr(), _stride(page_table, 0)
         a.pt_n_rows, a.pt_n_pages = page_table.shape[0], page_table.shape[1]
     a.page_size = page_size
     if row_req is not None:
@@ -262,7 +274,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
         if row_req.dim() != 1 or row_req.numel() != q.shape[0] or not row_req.is_contiguous():
             raise ValueError("row_req must be contiguous [n_rows]")
         a.row_req = row_req.data_ptr()
-    a.topk, a.topk_row_stride = topk.data_ptr(), topk.stride(0)
+    a.topk, a.topk_row_stride = topk.data_ptr(), _stride(topk, 0)
     a.k = topk.shape[1] if k is None else int(k)
     a.sm_scale = float(sm_scale)
     if out is not None:
@@ -270,7 +282,7 @@ def _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse
         if out.dim() != 3 or tuple(out.shape) != (q.shape[0], q.shape[1], LATENT) or out.stride(2) != 1 \
                 or out.stride(1) != LATENT:
             raise ValueError("out must be [n_rows, n_heads, 512] fp32 with heads packed")
-        a.out, a.out_row_stride = out.data_ptr(), out.stride(0)
+        a.out, a.out_row_stride = out.data_ptr(), _stride(out, 0)
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
         if tuple(lse.shape) != (q.shape[0], q.shape[1]) or not lse.is_contiguous():
@@ -357,10 +369,16 @@ def merge_states(part_o, part_lse, out=None, lse=None, stream=None):
         lse = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_o.device)
     _need(out, "out", torch.float32, part_o.device)
     _need(lse, "lse", torch.float32, part_o.device)
-    if not out.is_contiguous() or out.numel() != n_states * dim or not lse.is_contiguous() or lse.numel() != n_states:
-        raise ValueError("out / lse must be contiguous and match the parts")
+    if out.is_contiguous() and out.numel() == n_states * dim:
+        state_stride = dim
+    elif out.dim() == 2 and tuple(out.shape) == (n_states, dim) and out.stride(1) == 1 and out.stride(0) >= dim:
+        state_stride = out.stride(0)                 # rows of a wider array
+    else:
+        raise ValueError("out must be contiguous with the parts' shape, or [n_states, dim] with unit inner stride")
+    if not lse.is_contiguous() or lse.numel() != n_states:
+        raise ValueError("lse must be contiguous with one value per state")
     fn = load().kv4_merge_states_f16 if f16 else load().kv4_merge_states
-    _check(fn(_ptr(part_o), _ptr(part_lse), S, n_states, dim, _ptr(out), dim, _ptr(lse),
+    _check(fn(_ptr(part_o), _ptr(part_lse), S, n_states, dim, _ptr(out), state_stride, _ptr(lse),
               _stream(stream, part_o.device)))
     return out, lse
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "kv4.h"
 #include "kv4_launch.h"
@@ -60,6 +61,10 @@ kv4_status check_attn(const kv4_attn_args *a, bool need_out, bool need_q = true)
     if (a->k < 0) return fail(KV4_ERR_SHAPE, "k = %d < 0", a->k);
     if (a->k > KV4_MAX_K) return fail(KV4_ERR_UNSUPPORTED, "k = %d > %d", a->k, KV4_MAX_K);
     if (a->n_slots < 0) return fail(KV4_ERR_SHAPE, "n_slots < 0");
+    if (a->n_slots > 0x7FFFFFFF)   // slots are 32-bit inside the kernels
+        return fail(KV4_ERR_UNSUPPORTED, "n_slots = %lld; at most 2^31 - 1", (long long)a->n_slots);
+    if (need_q && !std::isfinite(a->sm_scale))
+        return fail(KV4_ERR_SHAPE, "sm_scale must be finite (got %g)", (double)a->sm_scale);
     if (a->n_rows == 0) return ok();
     if (need_q && !a->q) return fail(KV4_ERR_NULL, "q is NULL");
     if (a->k > 0 && !a->topk) return fail(KV4_ERR_NULL, "topk is NULL");

@@ -1,95 +1,108 @@
 // Sparse MLA attention over the 4-bit pool: decode (split-K) and prefill.
 //
 // README "60+ inference optimizations & kernels": section "4-bit KV cache"
-// (kv4mla dequantizes the 4-bit rows on chip instead of into an FP8 scratch
-// copy), section "AMD MI355X" (hand-written HIP sparse MLA decode whose K tile
-// in LDS is also the PV operand through a transposing LDS read; split-K
-// decode), "Parallelism and disaggregation" (per-part (o, lse) and a merge).
+// (the 4-bit rows are dequantized on chip, not into an FP8 scratch copy),
+// section "AMD MI355X" (hand-written HIP sparse MLA decode whose K tile in LDS
+// is also the P.V operand through a transposing LDS read; split-K decode),
+// "Parallelism and disaggregation" (per-part (o, lse) and their merge).
 // sgl-amd-mono GLM-5.3 PR, "Modifications": 64-token page table and its stride
-// as launch arguments; a split task serves many heads so each key row is
+// as launch arguments; one task serves many heads, so each key row is
 // gathered once per task.
 //
-// Workgroup = 4 wavefronts = (query row r, split s, chunk of up to 64 heads),
-// one per SIMD with the whole register file (queries and accumulators stay in
-// registers).  Wavefront w = (head group hg = w / 2 of 32 heads, half h = w %
-// 2).  Per tile of 32 list entries:
-//   1. the entries' pool slots (translated once per chunk of 2048 entries and
-//      kept in LDS) name 32 rows; lane t gathers row t % 32, bytes of part
-//      t / 32 (64 latent dims, their 4 scales, 8 rope dims) straight from HBM,
-//      two tiles ahead of the math;
-//   2. the lanes dequantize with gfx950's FP4/FP8 -> fp16 conversions at scale
-//      1 and one packed multiply by the E4M3 block scale (every product is exact
-//      in fp16) into a row-major K tile [32 rows][576] in LDS, double-buffered
-//      so this overlaps the previous tile's scores;
-//   3. wavefront (hg, h) computes the partial scores S^T[32 rows x 32 heads]
-//      over dims 288h..288h+287 with v_mfma_f32_32x32x16_f16 (queries in
-//      registers, pre-scaled per head by a power of two so they are exact in
-//      fp16), swaps partials with its partner through LDS, and accumulates
-//      O^T[256 dims x 32 heads] for latent dims 256h..256h+255 with the same
-//      MFMA from P = 2^(s - m_ref), where m_ref is the head's largest score in
-//      the first tile that has a valid entry (so the accumulators are never
-//      rescaled).  If a later score exceeds m_ref + 15 (P could overflow fp16)
-//      the workgroup runs the list again with m_ref = the exact maximum seen,
-//      which the first pass tracked.  P^T comes
-//      straight from the score registers and V^T from the K tile through
-//      ds_read_b64_tr_b16, which hands each lane a column of a row-major 4x16
-//      block.
-// The per-split result is written normalised with its lse; a split count of 1
-// writes the final output.
+// Workgroup = 8 wavefronts, two per SIMD, for one task (query row r, split s,
+// chunk of up to 64 heads), in two roles:
+//  - score wavefronts 0..3 = (head group hg = w % 2 of 32 heads, half = w / 2):
+//    the queries of 32 heads over half the dims in registers; per tile the
+//    partial scores S^T[32 rows x 32 heads] over those dims
+//    (v_mfma_f32_32x32x16_f16), swapped with the partner half through LDS so
+//    each owns 16 rows, and the softmax of those rows;
+//  - P.V wavefronts 4..7 = quarter dq of the 512 latent dims: O^T[128 dims x 64
+//    heads] accumulated from V^T (read from the same K tile through
+//    ds_read_b64_tr_b16) and the P of all 64 heads (LDS).
+// A SIMD holds one wavefront of each role, so per tile it issues 18 score and
+// 16 P.V MFMAs.  The roles exist because LDS bandwidth, not the MFMA pipe,
+// bounds this loop on gfx950 (stores about 78 B/clk per CU, plain reads about
+// 195 and transposing reads about 92 measured): keeping the queries and the
+// accumulators in different wavefronts lets each V^T and P element be read once
+// per tile and the score partials be split two ways only, for about 48 KB
+// written and 128 KB read per tile instead of 64 and 176.  The two roles run
+// their own loops, so each wavefront's registers hold only its role's state,
+// and they meet at the same barriers.
+// Per tile t, with three K tiles in rotation:
+//   phase 1: softmax of t (P to LDS) and scores of t + 1 (score wavefronts);
+//            dequantization of tile t + 2, latent dims 256..511 (P.V wavefronts)
+//   phase 2: P.V of t (P.V wavefronts); the partial-score swap of t + 1 and the
+//            dequantization of t + 2, latent dims 0..255 and the rope (score
+//            wavefronts)
+// with one barrier after each phase.  Gathering: the entries' pool slots
+// (translated once per chunk of 2048 entries, valid ones packed to the front,
+// kept in LDS) name 32 rows; thread t loads row t % 32, part t / 32 (32 latent
+// dims, their 2 block scales, 8 rope dims) four tiles ahead of its use, and
+// dequantizes with gfx950's FP4/FP8 -> fp16 conversions at scale 1 and one
+// packed multiply by the E4M3 block scale (every product is exact in fp16).
+// The softmax uses P = 2^(s - m_ref) with m_ref the head's largest score in
+// the first tile (agreed across the two halves); if a later score exceeds
+// m_ref + 15 (P could overflow fp16) the workgroup runs the list again with
+// m_ref = the exact maximum, which the first pass tracked.  The per-split
+// result is written normalised with its lse; a split count of 1 writes the
+// final output.
 //
 // Rows are either the 352-byte format (576 dims: 512 latent + 64 rope) or the
 // 288-byte rope-free format (512 latent dims; README, "4-bit KV cache": the
-// rope-free row of GLM-5.3-Flash).  The rope-free kernel is the same with 16
-// score k-steps per half instead of 18 and no rope to gather or decode; it
-// keeps the same slot schedule and LDS layout (the last 8 chunks of each K
-// tile unused).
+// rope-free row of GLM-5.3-Flash).
 #include "kv4_attn.h"
 #include "kv4_device.h"
 
 #include <type_traits>
 
+
 namespace kv4 {
 
+namespace {
+
+constexpr int kThreads = 512;                          // 8 wavefronts: 4 score, 4 P.V
 constexpr int kTile = 32;                              // list entries per tile
-constexpr int kKChunkBytes = 576;                      // one 16-byte chunk of the 32 rows + 4 slots
-constexpr int kKTileBytes = 72 * kKChunkBytes;         // 41472
-constexpr int kXBytes = 4 * 64 * 16 * 4;               // partial scores: 4 wavefronts x 64 lanes x 16
-constexpr int kSlotCap = 1024;                         // entries translated per chunk
-constexpr int kKBufs = 3;                              // K tiles in flight: P.V(t), scores(t+1), dequant(t+2)
-constexpr int kSlotOff = kKBufs * kKTileBytes + 2 * kXBytes + 16;
-constexpr int kCountOff = kSlotOff + kSlotCap * 4;   // valid entries per (batch, wavefront) of a chunk
-constexpr int kQmaxOff = kCountOff + 64;              // per-head query maxima of each wavefront
-constexpr int kLdsBytes = kQmaxOff + 4 * 32 * 4;      // 161872
+constexpr int kChunkB = 512;                           // one 8-dim chunk of a tile's 32 rows in fp16
+constexpr int kKTileB = 72 * kChunkB;                  // 36864: a K tile of 576 dims
+constexpr int kNBuf = 3;                               // K tiles in flight
+constexpr int kXB = 2 * 2 * 64 * 32;                   // partial scores: [hg][receiving half][lane] x 32 B
+constexpr int kPXHead = 80;                            // P of one head: 32 rows fp16 + 16 B pad
+constexpr int kPXB = 64 * kPXHead;
+constexpr int kSlotCap = 2048;                         // entries translated per chunk
+constexpr int kPosPerLane = kSlotCap / kThreads;
+constexpr int kOffX = kNBuf * kKTileB;                 // 110592
+constexpr int kOffPX = kOffX + kXB;                    // 118784
+constexpr int kOffSlots = kOffPX + kPXB;               // 123904
+constexpr int kOffCounts = kOffSlots + kSlotCap * 4;   // 132096
+constexpr int kOffRed = kOffCounts + kPosPerLane * 8 * 4;
+constexpr int kOffFlag = kOffRed + 2 * 2 * 32 * 4;
+constexpr int kLdsBytes = kOffFlag + 16;               // 132752
+constexpr int kStageBytes = kOffX;                     // the K tiles: staging of queries and outputs
+constexpr int kORow = kLatent + 4;                     // staged output row (floats; the pad spreads banks)
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
+static_assert(32 * kORow * 4 <= kStageBytes, "output staging overlaps the exchange");
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-// K-tile layout, chunk-major: element (row r, dim d) is at
-// (d / 8) * 576 + 16 r + 2 (d % 8), i.e. the 32 rows' copies of one 16-byte
-// chunk are contiguous, padded to 36 slots.  A score operand read (one chunk of
-// 32 rows per 32 lanes) and a dequantizing write (one chunk per 32 lanes) each
-// touch 512 contiguous bytes; a transposing read (4 rows x 4 chunks per 32
-// lanes) touches four 64-byte pieces whose 16-byte slots modulo 256 bytes are
-// 4q + 4g + j, all distinct because 36 = 4 mod 16.  gfx950's LDS serves each
-// at its full rate (256 bytes a clock for reads, 128 for writes) with no bank
-// conflict, and every address is a per-lane base plus a compile-time offset.
-constexpr int kcb(int chunk) { return chunk * kKChunkBytes; }
+// K-tile layout: element (row r, chunk c of 8 dims) at c * 512 + 16 * (r ^ 4 (c & 3)),
+// i.e. the 32 rows' copies of a 16-byte chunk are contiguous, their order
+// permuted by the chunk index.  A score operand read and a dequantizing write
+// (one chunk of 32 rows per 32 lanes) touch 512 contiguous bytes; a
+// transposing read (4 rows x 4 consecutive chunks per 32 lanes) touches 16
+// distinct 16-byte bank groups, because the XOR spreads the 4 chunks' copies of
+// a row over the 4 row groups.  No access pattern has a bank conflict and no
+// padding is needed.
+__device__ __forceinline__ uint32_t kswz(int r, int c) { return c * kChunkB + 16 * (r ^ (4 * (c & 3))); }
 
 __device__ __forceinline__ floatx16_t mfma32(half8_t a, half8_t b, floatx16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// LDS accesses by 32-bit byte address.  Each step pins (makes opaque to the
-// optimiser) one per-lane base per access pattern, so every access of the step
-// is that base plus a constant the instruction's offset field holds.
+// LDS accesses by 32-bit byte address.
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 __device__ __forceinline__ uint32_t lds_addr(uint8_t *p) { return (uint32_t)(size_t)(lds_u8_t *)p; }
-__device__ __forceinline__ uint32_t pin(uint32_t v) {
-    asm("" : "+v"(v));
-    return v;
-}
 template <typename T>
 __device__ __forceinline__ T lds_ld(uint32_t a) {
     return *(const __attribute__((address_space(3))) T *)(size_t)a;
@@ -102,63 +115,10 @@ __device__ __forceinline__ short4_t lds_read_tr16(uint32_t a) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t *)(size_t)a);
 }
 
-// One lane's share of a tile's rows: row t % 32, part t / 32 (latent dims
-// 64 part .. +63 as 32 code bytes, their 4 block scales, rope dims 8 part .. +7).
-struct RowPart {
-    u32x4_t c0, c1;
-    uint32_t sc;
-    u32x2_t rp;
-    bool valid;
-};
-
-// A skipped entry reads 352 readable bytes elsewhere (`stand_in`: the query
-// row, at least 1152 bytes, so an empty pool is never touched) and is zeroed by
-// dequant_part: scale and rope bytes become 0, so every value is 0.
-// Row layout: 352 bytes with the 64 rope values, or the 288-byte rope-free
-// row (codes and scales only, README "60+ inference optimizations & kernels",
-// section "4-bit KV cache": GLM-5.3-Flash's rope-free row).
 template <bool ROPE>
 constexpr int row_bytes() { return ROPE ? kRowBytes : kScaleOff + kLatent / 16; }
 
-template <bool ROPE>
-__device__ __forceinline__ void gather_part(const uint8_t *__restrict__ pool, const uint8_t *stand_in, int32_t slot,
-                                            int gp, RowPart &R) {
-    R.valid = slot >= 0;
-    const uint8_t *row = R.valid ? pool + (int64_t)slot * row_bytes<ROPE>() : stand_in;
-    R.c0 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp);
-    R.c1 = *reinterpret_cast<const u32x4_t *>(row + 32 * gp + 16);
-    R.sc = *reinterpret_cast<const uint32_t *>(row + kScaleOff + 4 * gp);
-    if constexpr (ROPE) R.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * gp);
-    else R.rp = u32x2_t{0, 0};
-}
-
-// dq = the lane's row in its part's first latent chunk (chunk 8 * part), rq =
-// the lane's row in its rope chunk (chunk 64 + part)
-template <bool ROPE>
-__device__ __forceinline__ void dequant_part(uint32_t dq, uint32_t rq, const RowPart &R) {
-    const uint32_t sc = R.valid ? R.sc : 0u;
-    const u32x2_t rp = R.valid ? R.rp : u32x2_t{0, 0};
-    half2_t d[4];
-    block_scales_half_cvt(sc, d);
-    const uint32_t c[8] = {R.c0[0], R.c0[1], R.c0[2], R.c0[3], R.c1[0], R.c1[1], R.c1[2], R.c1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t v[4];
-        e2m1x8_to_half_cvt(c[i], d[i >> 1], v);
-        lds_st<u32x4_t>(dq + kcb(i), u32x4_t{v[0], v[1], v[2], v[3]});
-    }
-    if constexpr (ROPE) {
-        uint32_t h[4];
-        e4m3x4_to_half_cvt(rp[0], h);
-        e4m3x4_to_half_cvt(rp[1], h + 2);
-        lds_st<u32x4_t>(rq, u32x4_t{h[0], h[1], h[2], h[3]});
-    }
-}
-
-constexpr int kPosPerLane = kSlotCap / 256;
-
-// f(integral_constant<int, I>) for I = B .. E-1, each with its index known at
-// compile time (a plain loop this large is not unrolled by the compiler)
+// f(integral_constant<int, I>) for I = B .. E-1, each index known at compile time
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     if constexpr (B < E) {
@@ -167,29 +127,168 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-template <bool QF32, bool ROPE>
-__global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
-    // row format: K has kD dims (latent + rope, or latent only); each half of
-    // the scores covers kD / 2 of them in kSteps MFMA k-steps of 16
-    constexpr int kD = ROPE ? kDim : kLatent;
-    constexpr int kSteps = kD / 32;
-    constexpr int kHalfChunks = kD / 16;
-    constexpr int kRowB = row_bytes<ROPE>();
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    int32_t *redo = reinterpret_cast<int32_t *>(lds + kKBufs * kKTileBytes + 2 * kXBytes);
-    int32_t *slots = reinterpret_cast<int32_t *>(lds + kSlotOff);
-    int32_t *counts = reinterpret_cast<int32_t *>(lds + kCountOff);
-    float *qmx = reinterpret_cast<float *>(lds + kQmaxOff);
-    const uint32_t kb0 = lds_addr(lds);
+// ------------------------------------------------ translation of a list chunk
+// Shared by the attention kernel and the gather test entry point, which must
+// run the same code.  Thread t holds list entries c_lo + t + 512 i.
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = blockIdx.x, split = blockIdx.y;
-    const int hg = blockIdx.z * 2 + (wave >> 1);
-    const int half = wave & 1;
+struct ListCtx {
+    const int32_t *list;      // this query row's list
+    const int32_t *pt_row;    // its page-table row; null without a page table or for a bad request
+    bool bad_req;             // a page table is given but the row's request is outside it
+};
+
+__device__ __forceinline__ ListCtx list_ctx(const AttnParams &p, int r) {
+    ListCtx c;
+    const int32_t req = p.row_req ? p.row_req[r] : r;
+    c.bad_req = p.page_table && (req < 0 || req >= p.pt_n_rows);
+    c.pt_row = p.page_table && !c.bad_req ? p.page_table + (int64_t)req * p.pt_row_stride : nullptr;
+    c.list = p.topk + (int64_t)r * p.topk_row_stride;
+    return c;
+}
+
+__device__ __forceinline__ void load_positions(const ListCtx &c, int c_lo, int c_hi, int tid, int32_t (&pos)[kPosPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kPosPerLane; ++i) {
+        const int e = c_lo + tid + kThreads * i;
+        pos[i] = e < c_hi ? c.list[e] : -1;
+    }
+}
+
+__device__ __forceinline__ void load_pages(const AttnParams &p, const ListCtx &c, const int32_t (&pos)[kPosPerLane],
+                                           int32_t (&phys)[kPosPerLane]) {
+#pragma unroll
+    for (int i = 0; i < kPosPerLane; ++i) {
+        phys[i] = -1;
+        if (c.pt_row && pos[i] >= 0 && (pos[i] >> p.page_shift) < p.pt_n_pages) phys[i] = c.pt_row[pos[i] >> p.page_shift];
+    }
+}
+
+// Packs the valid entries' slots, in list order, to the front of slots[] and
+// pads with -1 up to a whole number of tile pairs (64 entries); returns the
+// number of valid entries (the same in every thread).  Holds a barrier, so every thread calls it; the caller
+// synchronizes before slots[] is read.
+__device__ __forceinline__ int pack_slots(const AttnParams &p, const ListCtx &c, const int32_t (&pos)[kPosPerLane],
+                                          const int32_t (&phys)[kPosPerLane], int tid, int32_t *slots,
+                                          int32_t *counts, uint32_t &err) {
+    const int lane = tid & 63, w = tid >> 6;
+    int32_t sl[kPosPerLane];
+    uint64_t bal[kPosPerLane];
+#pragma unroll
+    for (int i = 0; i < kPosPerLane; ++i) {   // entry tid + 512 i: list order is (i, wavefront, lane)
+        int64_t s = -1;
+        if (c.bad_req) err |= pos[i] >= 0 ? kErrPage : 0u;
+        else s = slot_of(pos[i], phys[i], c.pt_row != nullptr, p.pt_n_pages, p.page_shift, p.n_slots, err);
+        sl[i] = (int32_t)s;                   // s < n_slots <= 2^31 - 1
+        bal[i] = __ballot(s >= 0);
+        if (lane == 0) counts[8 * i + w] = (int32_t)__popcll(bal[i]);
+    }
+    __syncthreads();
+    int nv = 0, base[kPosPerLane];
+#pragma unroll
+    for (int i = 0; i < kPosPerLane; ++i) {
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+            if (ww == w) base[i] = nv;
+            nv += counts[8 * i + ww];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPosPerLane; ++i) {
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u));
+        if (sl[i] >= 0) slots[base[i] + below] = sl[i];
+        const int e = tid + kThreads * i;
+        if (e >= nv && e < ((nv + 2 * kTile - 1) & ~(2 * kTile - 1))) slots[e] = -1;
+    }
+    return nv;
+}
+
+// ------------------------------------------------ gather and dequantization
+// Thread t takes row gr = t % 32 of a tile and part gp = t / 32: code bytes
+// 16gp .. 16gp + 15 (latent dims 32gp .. 32gp + 31, K-tile chunks 4gp .. 4gp +
+// 3), block scales 2gp and 2gp + 1 (from the aligned word of scales 4(gp/2) ..
+// + 3), and (parts 0..7, the score wavefronts' threads, when WITH_ROPE) rope
+// bytes 8gp .. 8gp + 7 (chunk 64 + gp).  A skipped
+// entry (slot < 0) reads 352 readable bytes elsewhere (`stand_in`) and
+// dequantizes to zeros: its scale and rope bytes become 0.  The loads take no
+// branch, so the compiler can count them and wait for exactly the set it needs.
+
+template <bool ROPE>
+struct GSet {
+    u32x4_t c;
+    uint32_t sc;
+    u32x2_t rp;
+    bool valid;
+};
+
+template <bool ROPE, bool WITH_ROPE = ROPE>
+__device__ __forceinline__ void gather_set(const uint8_t *__restrict__ pool, const uint8_t *stand_in, int32_t slot,
+                                           int gp, GSet<ROPE> &G) {
+    G.valid = slot >= 0;
+    const uint8_t *row = pool + (int64_t)max(slot, 0) * row_bytes<ROPE>();
+    row = G.valid ? row : stand_in;
+    G.c = *reinterpret_cast<const u32x4_t *>(row + 16 * gp);
+    G.sc = *reinterpret_cast<const uint32_t *>(row + kScaleOff + 4 * (gp >> 1));   // scales 4(gp/2) .. +3
+    if constexpr (WITH_ROPE) G.rp = *reinterpret_cast<const u32x2_t *>(row + kRopeOff + 8 * (gp & 7));
+    else G.rp = u32x2_t{0, 0};
+}
+
+// rope_part: this wavefront stores the rope chunk (wave-uniform: wavefronts 0..3)
+template <bool ROPE>
+__device__ __forceinline__ void dequant_set(uint32_t kb, int gr, int gp, bool rope_part, const GSet<ROPE> &G) {
+    const uint32_t sc = G.valid ? G.sc >> (16 * (gp & 1)) : 0u;                     // this part's two scales
+    const half2_t dd = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);   // E4M3 -> fp16, exact
+    const half2_t d0 = __builtin_shufflevector(dd, dd, 0, 0), d1 = __builtin_shufflevector(dd, dd, 1, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {             // chunk 4gp + i: dims 32gp + 8i .. +7, block 2gp + i / 2
+        const uint32_t wv = G.c[i];
+        const half2_t d = i < 2 ? d0 : d1;
+        u32x4_t v;
+        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 0) * d);
+        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 1) * d);
+        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 2) * d);
+        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 3) * d);
+        lds_st<u32x4_t>(kb + kswz(gr, 4 * gp + i), v);
+    }
+    if constexpr (ROPE) {
+        if (rope_part) {
+            const u32x2_t rp = G.valid ? G.rp : u32x2_t{0, 0};
+            u32x4_t h;
+            h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, false));
+            h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, true));
+            h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, false));
+            h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, true));
+            lds_st<u32x4_t>(kb + kswz(gr, 64 + gp), h);
+        }
+    }
+}
+
+}  // namespace
+
+template <bool QF32, bool ROPE>
+__global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
+    // K has kD dims (latent + rope, or latent only); a score wavefront's half
+    // of them is kHd dims = kKs MFMA k-steps of 16 = kHc chunks of 8
+    constexpr int kD = ROPE ? kDim : kLatent;
+    constexpr int kHd = kD / 2;
+    constexpr int kKs = kHd / 16;
+    constexpr int kHc = kHd / 8;
+    constexpr int kAhead = QF32 ? 2 : 4;       // score operands read ahead of their MFMA
+    constexpr int kTrAhead = 4;                // P.V operand pairs read ahead
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + kOffSlots);
+    int32_t *counts = reinterpret_cast<int32_t *>(lds + kOffCounts);
+    float *red = reinterpret_cast<float *>(lds + kOffRed);
+    int32_t *flag = reinterpret_cast<int32_t *>(lds + kOffFlag);
+    const uint32_t L = lds_addr(lds);
+
+    // wavefront-uniform values live in scalar registers, so the branches on
+    // them are scalar and no lane mask is ever saved and restored
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int head = hg * 32 + l32;
-    const bool group_live = hg * 32 < p.n_heads;
-    const bool head_live = head < p.n_heads;
+    const int gr = tid & 31, gp = tid >> 5;
+    const int r = blockIdx.x, split = blockIdx.y, h0 = blockIdx.z * 64;
 
     const int n_tiles = (p.k + kTile - 1) / kTile;
     const int t_lo = split * p.tiles_per_split;
@@ -197,520 +296,576 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(AttnParams p) {
     const int e_lo = t_lo * kTile;
     const int e_hi = min(p.k, t_hi * kTile);
 
-    const int32_t req = p.row_req ? p.row_req[r] : r;
-    const bool bad_req = p.page_table && (req < 0 || req >= p.pt_n_rows);
-    const int32_t *pt_row = p.page_table && !bad_req ? p.page_table + (int64_t)req * p.pt_row_stride : nullptr;
-    const int32_t *list = p.topk + (int64_t)r * p.topk_row_stride;
+    const ListCtx lc = list_ctx(p, r);
+    const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
     uint32_t err = 0;
 
-    // Translation of a chunk of at most kSlotCap entries: the list entries
-    // first, then their page-table entries, each batch issued before any of it
-    // is used.  write_slots packs the valid entries' slots, in list order, to
-    // the front of slots[] and pads the last tile with -1, so every tile but
-    // the last is full; it returns the number of valid entries (the same in
-    // every thread) and holds a barrier, so all threads call it.
-    int32_t pos[kPosPerLane], phys[kPosPerLane];
-    auto load_positions = [&](int c_lo, int c_hi) {
+    // ---- Prologue, arranged so its memory round trips overlap: the first
+    // chunk's list entries, this row's queries (coalesced: consecutive threads
+    // take consecutive 16-byte chunks of a head's row), the page-table entries
+    // once the list is back, the queries staged in LDS (the K tiles are not in
+    // use yet; rows padded so the fragment reads are conflict-free), the slots.
+    // bf16 queries are staged at once; fp32 ones in two rounds, one per head
+    // group.
+    constexpr int kQE = QF32 ? 4 : 2;                      // bytes per query element
+    constexpr int kQRow = kD * kQE + 16;                   // staged head row
+    constexpr int kQH = QF32 ? 32 : 64;                    // heads staged per round
+    constexpr int kQChunks = kD * kQE / 16;                // 16-byte chunks per head row
+    constexpr int kQPer = kQH * kQChunks / kThreads;       // chunks per thread
+    static_assert(kQH * kQChunks % kThreads == 0, "query chunks do not divide");
+    static_assert(kQH * kQRow <= kStageBytes, "staged queries overlap the exchange");
+    const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * kQE;
+    auto load_q = [&](int round, u32x4_t (&qc)[kQPer]) {
 #pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {
-            const int e = tid + 256 * i;
-            pos[i] = c_lo + e < c_hi ? list[c_lo + e] : -1;
+        for (int i = 0; i < kQPer; ++i) {
+            const int c = tid + kThreads * i, hh = c / kQChunks, part = c % kQChunks;
+            const int head = h0 + kQH * round + hh;
+            qc[i] = u32x4_t{0, 0, 0, 0};
+            if (head < p.n_heads)
+                qc[i] = *reinterpret_cast<const u32x4_t *>(qr + (int64_t)head * p.q_head_stride * kQE + 16 * part);
         }
     };
-    auto load_pages = [&]() {
+    auto stage_q = [&](const u32x4_t (&qc)[kQPer]) {
 #pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {
-            phys[i] = -1;
-            if (pt_row && pos[i] >= 0 && (pos[i] >> p.page_shift) < p.pt_n_pages) phys[i] = pt_row[pos[i] >> p.page_shift];
+        for (int i = 0; i < kQPer; ++i) {
+            const int c = tid + kThreads * i, hh = c / kQChunks, part = c % kQChunks;
+            lds_st<u32x4_t>(L + hh * kQRow + 16 * part, qc[i]);
         }
-    };
-    auto write_slots = [&]() -> int {
-        int32_t sl[kPosPerLane];
-        uint64_t bal[kPosPerLane];
-#pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {       // entry e = tid + 256 i: list order is (i, wave, lane)
-            int64_t s = -1;
-            if (bad_req) err |= pos[i] >= 0 ? kErrPage : 0u;
-            else s = slot_of(pos[i], phys[i], pt_row != nullptr, p.pt_n_pages, p.page_shift, p.n_slots, err);
-            sl[i] = (int32_t)s;
-            bal[i] = __ballot(s >= 0);
-            if (lane == 0) counts[4 * i + wave] = (int32_t)__popcll(bal[i]);
-        }
-        __syncthreads();
-        int nv = 0, base[kPosPerLane];
-#pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (w == wave) base[i] = nv;
-                nv += counts[4 * i + w];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kPosPerLane; ++i) {
-            const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u));
-            if (sl[i] >= 0) slots[base[i] + below] = sl[i];
-            const int e = tid + 256 * i;
-            if (e >= nv && e < ((nv + kTile - 1) & ~(kTile - 1))) slots[e] = -1;
-        }
-        return nv;
     };
 
-    // ---- Prologue, arranged so its memory round trips overlap: the first
-    // chunk's list entries, then this workgroup's queries (coalesced:
-    // consecutive lanes take consecutive 16-byte chunks of a head's row), the
-    // page-table entries once the list is back, the queries staged in LDS (the
-    // K-tile buffers are not in use yet; rows padded so the fragment reads
-    // below are conflict-free), and the slots.  The query fragments are read,
-    // scaled and converted in the first chunk's prologue, while its first
-    // tiles are being gathered.
-    constexpr int kQElem = QF32 ? 4 : 2;
-    constexpr int kQChunks = kD * kQElem / 16;             // 16-byte chunks per head row
-    constexpr int kQRow = kD * kQElem + 16;                // staged head row (at most 2320 bytes)
-    constexpr int kQPer = 64 * kQChunks / 256;             // chunks per thread
-    static_assert(64 * kQRow <= kSlotOff - 16, "staged queries overlap the slot list");
+    int32_t pos[kPosPerLane], phys[kPosPerLane];
     const int first_hi = min(e_hi, e_lo + kSlotCap);
-    if (e_lo < e_hi) load_positions(e_lo, first_hi);       // issued first: loads complete in order
-    else load_positions(0, 0);
-    {
-        const int h0 = blockIdx.z * 64;
-        const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * kQElem;
-        u32x4_t qc[kQPer];
-#pragma unroll
-        for (int i = 0; i < kQPer; ++i) {
-            const int c = tid + 256 * i, hh = c / kQChunks, part = c % kQChunks;
-            qc[i] = u32x4_t{0, 0, 0, 0};
-            if (h0 + hh < p.n_heads)
-                qc[i] = *reinterpret_cast<const u32x4_t *>(qr + (int64_t)(h0 + hh) * p.q_head_stride * kQElem + 16 * part);
-        }
-        if (e_lo < e_hi) load_pages();
-#pragma unroll
-        for (int i = 0; i < kQPer; ++i) {
-            const int c = tid + 256 * i, hh = c / kQChunks, part = c % kQChunks;
-            lds_st<u32x4_t>(kb0 + hh * kQRow + 16 * part, qc[i]);
-        }
-    }
-    int nv = e_lo < e_hi ? write_slots() : 0;      // valid entries of the current chunk (holds a barrier)
-    if (tid == 0) *redo = 0;                       // set only in pass 0; read after its last barrier
+    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);   // issued first: loads complete in order
+    u32x4_t qc[kQPer];
+    load_q(0, qc);
+    load_pages(p, lc, pos, phys);
+    stage_q(qc);
+    int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
+    if (tid == 0) *flag = 0;
     __syncthreads();
 
-    // ---- queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head l32,
-    // dims 288*half + 16ks + 8g .. +7 for ks = 0..17.  The power-of-two scale
-    // qs puts the head's largest |q| in [2^13, 2^14): exact in fp16 (fp32
-    // queries: a hi and a lo fp16 part).  Run once, with a barrier, by every
-    // thread (the largest |q| of the head's other half comes from the partner
-    // wavefront through LDS).
-    half8_t qb[kSteps];
-    half8_t ql[QF32 ? kSteps : 1];
-    float score_mul = 0.0f;
-    auto convert_queries = [&]() {
-        const uint32_t qf = kb0 + ((wave >> 1) * 32 + l32) * kQRow + (kD / 2 * half + 8 * g) * kQElem;
-        float qmax = 0.0f;
-        if constexpr (QF32) {
-            floatx4_t v[2 * kSteps];
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks) {
-                v[2 * ks] = lds_ld<floatx4_t>(qf + 64 * ks);
-                v[2 * ks + 1] = lds_ld<floatx4_t>(qf + 64 * ks + 16);
-            }
-#pragma unroll
-            for (int i = 0; i < 2 * kSteps; ++i)
-                qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[i][0]), __builtin_fabsf(v[i][1])),
-                                                             __builtin_fmaxf(__builtin_fabsf(v[i][2]), __builtin_fabsf(v[i][3]))));
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
-            if (g == 0) qmx[wave * 32 + l32] = qmax;
-            __syncthreads();
-            qmax = __builtin_fmaxf(qmax, qmx[(wave ^ 1) * 32 + l32]);
-            int ex = 0;
-            if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
-            const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
-            score_mul = p.score_mul / qs;
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = v[2 * ks + (e >> 2)][e & 3] * qs;
-                    const _Float16 hi = (_Float16)x;
-                    qb[ks][e] = hi;
-                    ql[ks][e] = (_Float16)(x - (float)hi);
-                }
-        } else {
-            u32x4_t v[kSteps];
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks) v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[ks][c] << 16)),
-                                                                 __builtin_fabsf(__uint_as_float(v[ks][c] & 0xFFFF0000u))));
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
-            if (g == 0) qmx[wave * 32 + l32] = qmax;
-            __syncthreads();
-            qmax = __builtin_fmaxf(qmax, qmx[(wave ^ 1) * 32 + l32]);
-            int ex = 0;
-            if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
-            const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
-            score_mul = p.score_mul / qs;
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    qb[ks][2 * c] = (_Float16)(__uint_as_float(v[ks][c] << 16) * qs);
-                    qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[ks][c] & 0xFFFF0000u) * qs);
-                }
-        }
+    const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
+    int n_t = 0, n_real = 0, last_rows = kTile;   // tiles (even), tiles holding entries, rows of the last
+    bool have_ref = false;                         // uniform: the softmax reference is set
+    // the chunk's tile counts after its slots are packed (the same in every thread)
+    auto chunk_tiles = [&]() {
+        n_real = (nv + kTile - 1) / kTile;
+        n_t = (n_real + 1) & ~1;
+        last_rows = nv - kTile * (n_real - 1);
     };
-
-    floatx16_t o[8];
-    float m_ref = -__builtin_inff();   // reference of P = 2^(s - m_ref) for this lane's head
-    float m_max = -__builtin_inff();   // largest score seen (the exact maximum after a pass)
-    float l_run = 0.0f;
-
-    const int gr = tid & 31, gp = tid >> 5;        // gather role: row gr, part gp
-    const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
-    // per-lane offsets inside a K tile:
-    //  score operand: row l32 of chunk 36*half + 2ks + g
-    const uint32_t qk_off = kcb(kHalfChunks * half + g) + 16 * l32;
-    //  transposing reads: this lane supplies row 4g + (lane&15)/4 (+8 for the
-    //  second read of a k-half, +16 for the second k-half), 8 bytes at latent
-    //  dims 256*half + 32*md + 16*((lane>>4)&1) + 4*(lane&3)
-    const uint32_t tr_off = kcb(32 * half + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) +
-                            16 * (4 * g + ((lane >> 2) & 3)) + 8 * (lane & 1);
-    //  dequantized row gr, part gp: latent chunks 8gp..8gp+7 and rope chunk 64+gp
-    const uint32_t dq_off = kcb(8 * gp) + 16 * gr;
-    const uint32_t rope_off = kcb(64 + gp) + 16 * gr;
-    // exchange buffers: wavefront w's partial of register group q4 for lane l
-    // at (w*4 + q4)*64 + l (16 bytes each); buffer xb at xb * kXBytes
-    const uint32_t x_own = pin(kb0 + kKBufs * kKTileBytes + wave * 4096 + 16 * lane);
-    const uint32_t x_partner = pin(kb0 + kKBufs * kKTileBytes + (wave ^ 1) * 4096 + 16 * lane);
-
-    // partial scores S^T over this half's 288 dims for the K tile at sb (=
-    // tile + qk_off), written to exchange buffer xb (one accumulator chain;
-    // fp32 queries add their lo parts into the same chain)
-    auto scores_to_x = [&](uint32_t sb, int xb) {
-        floatx16_t sacc = {};
-#pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks) {
-            const half8_t a = lds_ld<half8_t>(sb + kcb(2 * ks));
-            sacc = mfma32(a, qb[ks], sacc);
-            if constexpr (QF32) sacc = mfma32(a, ql[ks], sacc);
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            lds_st<floatx4_t>(x_own + xb * kXBytes + 1024 * q4,
-                              floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
-    };
-
-    // P of tile t from exchange buffer xb: own + partner partial scores,
-    // P = 2^(s - m_ref) as the two fp16 B operands of P.V; updates l_run (the
-    // sum of the fp16 P that P.V uses), m_ref, m_max.  The chunk's last tile
-    // takes the masked form, where the padding rows' scores become -inf.
-    half8_t pb0 = {}, pb1 = {};
-    bool need_redo = false;
-    int last_rows = kTile;                             // valid rows of the chunk's last tile
-    // Steady state, iteration t (one barrier), laid out by hand as 34 MFMA
-    // slots: 18 score MFMAs of tile t+1 (K tile at bB, into exchange buffer
-    // xb^1; 36 for fp32 queries) then 16 P.V MFMAs of tile t (bA), the first
-    // half of P first.  The scheduler is fenced (sched_barrier) after every
-    // slot, so operand reads stay a few MFMAs ahead and each slot's other
-    // work sits beside its MFMA.  That work is spread evenly because a
-    // wavefront issues in order (a value that is not ready stalls it) and
-    // gfx950's LDS takes writes at about 64 bytes a clock per CU:
-    //  - the softmax of tile t (exchange buffer xb): sums, a max tree, then
-    //    fma -> exp -> fp16 -> row sums, one step per slot;
-    //  - the dequantization of tile t+2 (rows held in cur, into bC): chunk i
-    //    converted in one slot, scaled and stored a slot later, a store every
-    //    four slots, interleaved with the four stores of the new scores;
-    //  - the gather of tile t+4 into cur, each piece as soon as its
-    //    registers are free.
-    // Past the chunk's end the scores, dequant and gather work on stale
-    // buffers nobody reads (the gather index is clamped to a real tile).
-    auto iteration = [&](auto masked, int t, int n_t, RowPart &cur, uint32_t bA, uint32_t bB, uint32_t bC, int xb) {
-        constexpr int kAhead = 4;                     // score operand reads in flight
-        constexpr int kTrAhead = 3;                   // P.V operand pairs in flight
-        const uint32_t sb = pin(bB + qk_off), tb = pin(bA + tr_off);
-        const uint32_t dq = pin(bC + dq_off), rq = pin(bC + rope_off);
-        const int32_t next_slot = slots[min(t + 4, n_t - 1) * kTile + gr];
-        floatx4_t xo[4], xq[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            xo[q4] = lds_ld<floatx4_t>(x_own + xb * kXBytes + 1024 * q4);
-            xq[q4] = lds_ld<floatx4_t>(x_partner + xb * kXBytes + 1024 * q4);
-        }
-        half8_t ka[kAhead];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) ka[i] = lds_ld<half8_t>(sb + kcb(2 * i));
-        __builtin_amdgcn_sched_barrier(0);
-
-        short4_t tlo[kTrAhead], thi[kTrAhead];
-        auto tr_issue = [&](int j) {                  // P.V MFMA j: k-half kk = j / 8, dims block md = j % 8
-            const int md = j & 7, kk = j >> 3;
-            tlo[j % kTrAhead] = lds_read_tr16(tb + kcb(4 * md) + 16 * (16 * kk));
-            thi[j % kTrAhead] = lds_read_tr16(tb + kcb(4 * md) + 16 * (16 * kk + 8));
-        };
-        float raw[16], mx[7], e[16], ls[4];
-        float tmax = 0.0f, nmr = 0.0f;
-        uint32_t sw0 = 0, sw1 = 0, sc_sel = 0, cv[2][4], rh[4];
-        u32x2_t rp_sel = {0, 0};
-        half2_t d[4];
-        const uint8_t *nrow = stand_in;
-        bool nvalid = false;
-        const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-        auto cvt_chunk = [&](int i) {                 // E2M1 codes of latent chunk i -> fp16 at scale 1
-            const uint32_t w = i < 4 ? cur.c0[i] : cur.c1[i - 4];
-            cv[i & 1][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
-            cv[i & 1][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
-            cv[i & 1][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
-            cv[i & 1][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
-        };
-        auto scale_store = [&](int i) {               // times the block scale, to the K tile
-            const half2_t di = d[i >> 1];
-            lds_st<u32x4_t>(dq + kcb(i), u32x4_t{__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][0]) * di),
-                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][1]) * di),
-                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][2]) * di),
-                                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, cv[i & 1][3]) * di)});
-        };
-        auto x_store = [&](const floatx16_t &sacc, int q4) {   // new scores for the partner
-            lds_st<floatx4_t>(x_own + (xb ^ 1) * kXBytes + 1024 * q4,
-                              floatx4_t{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]});
-        };
-        floatx16_t sacc = {};
-        // The softmax of tile t delivers P in slots 16 and 17, so P.V starts at
-        // slot 18 in both row formats; the rope-free scores take slots 0..15
-        // and leave 16 and 17 without an MFMA.
-        static_for<0, 34>([&](auto slot) {
-            constexpr int s = decltype(slot)::value;
-            // ---- the MFMA of the slot and the operand reads ahead of it
-            if constexpr (s < kSteps) {
-                sacc = mfma32(ka[s % kAhead], qb[s], sacc);
-                if constexpr (QF32) sacc = mfma32(ka[s % kAhead], ql[s], sacc);
-                if constexpr (s + kAhead < kSteps) ka[s % kAhead] = lds_ld<half8_t>(sb + kcb(2 * (s + kAhead)));
-            } else if constexpr (s >= 18) {
-                constexpr int j = s - 18, md = j & 7, kk = j >> 3;
-                const half8_t a = __builtin_bit_cast(
-                    half8_t, __builtin_shufflevector(tlo[j % kTrAhead], thi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
-                o[md] = mfma32(a, kk ? pb1 : pb0, o[md]);
-                if constexpr (j + kTrAhead < 16) tr_issue(j + kTrAhead);
-            }
-            if constexpr (s >= 18 - kTrAhead && s < 18) tr_issue(s - (18 - kTrAhead));
-            // ---- softmax of tile t
-            if constexpr (s == 1 || s == 2) {                   // own + partner partial scores
-#pragma unroll
-                for (int q4 = 2 * (s - 1); q4 < 2 * s; ++q4)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) raw[4 * q4 + i] = xo[q4][i] + xq[q4][i];
-            }
-            if constexpr (s == 2) {
-                if constexpr (decltype(masked)::value) {   // the chunk's last tile: rows >= last_rows are padding
-                    const int lim = last_rows - 4 * g;      // register v holds row 8(v/4) + 4g + v%4
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (8 * (v >> 2) + (v & 3) >= lim) raw[v] = -__builtin_inff();
-                }
-            }
-            if constexpr (s == 3) {                             // row maximum as a tree
-#pragma unroll
-                for (int i = 0; i < 5; ++i)
-                    mx[i] = __builtin_fmaxf(__builtin_fmaxf(raw[3 * i], raw[3 * i + 1]), raw[3 * i + 2]);
-            }
-            if constexpr (s == 4) {
-                mx[5] = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), mx[2]);
-                mx[6] = __builtin_fmaxf(__builtin_fmaxf(mx[3], mx[4]), raw[15]);
-            }
-            if constexpr (s == 5) {                             // lanes l and l ^ 32 hold the same head
-                const float rm = __builtin_fmaxf(mx[5], mx[6]);
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rm), __float_as_uint(rm), false, false);
-                sw0 = sw[0];
-                sw1 = sw[1];
-            }
-            if constexpr (s == 6) tmax = __builtin_fmaxf(__uint_as_float(sw0), __uint_as_float(sw1)) * score_mul;   // score_mul > 0
-            if constexpr (s == 7) {
-                m_max = __builtin_fmaxf(m_max, tmax);
-                if (m_ref == -__builtin_inff()) m_ref = tmax;    // first tile with a valid entry
-                need_redo |= tmax > m_ref + kRefSlack;           // P could overflow fp16 (pass 0 only)
-                nmr = m_ref == -__builtin_inff() ? 0.0f : -m_ref;   // nothing valid so far
-            }
-            if constexpr (s >= 8 && s < 16) {                   // exponent of two values, 2^ of the previous two
-                constexpr int u = s - 8;
-                if constexpr (u > 0) {
-                    e[2 * u - 2] = __builtin_amdgcn_exp2f(e[2 * u - 2]);   // exp2(-inf) = 0
-                    e[2 * u - 1] = __builtin_amdgcn_exp2f(e[2 * u - 1]);
-                }
-                e[2 * u] = __builtin_fmaf(raw[2 * u], score_mul, nmr);
-                e[2 * u + 1] = __builtin_fmaf(raw[2 * u + 1], score_mul, nmr);
-            }
-            if constexpr (s == 16) {
-                e[14] = __builtin_amdgcn_exp2f(e[14]);
-                e[15] = __builtin_amdgcn_exp2f(e[15]);
-#pragma unroll
-                for (int v = 0; v < 8; ++v) pb0[v] = (_Float16)e[v];
-            }
-            if constexpr (s == 17) {
-#pragma unroll
-                for (int v = 0; v < 8; ++v) pb1[v] = (_Float16)e[8 + v];
-            }
-            if constexpr (s == 18 || s == 19) {                 // l += the fp16 P that P.V uses: four partial sums
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const half2_t pp = s == 18 ? half2_t{pb0[2 * i], pb0[2 * i + 1]} : half2_t{pb1[2 * i], pb1[2 * i + 1]};
-                    ls[i] = __builtin_amdgcn_fdot2(pp, one2, s == 18 ? 0.0f : ls[i], false);
-                }
-            }
-            if constexpr (s == 20) {
-                ls[0] += ls[1];
-                ls[2] += ls[3];
-            }
-            if constexpr (s == 21) ls[0] += ls[2];
-            if constexpr (s == 22) l_run += ls[0];
-            // ---- dequantization of tile t+2
-            if constexpr (s == 0) {                             // a skipped entry dequantizes to zeros
-                sc_sel = cur.valid ? cur.sc : 0u;
-                rp_sel = cur.valid ? cur.rp : u32x2_t{0, 0};
-                block_scales_half_cvt(sc_sel, d);
-            }
-            constexpr int ci = s >= 1 && (s - 1) % 4 == 0 && (s - 1) / 4 < 8 ? (s - 1) / 4 : -1;
-            constexpr int si = s >= 2 && (s - 2) % 4 == 0 && (s - 2) / 4 < 8 ? (s - 2) / 4 : -1;
-            if constexpr (ci >= 0) cvt_chunk(ci);    // chunk i converted in slot 1 + 4i
-            if constexpr (si >= 0) scale_store(si);  // and stored a slot later
-            if constexpr (ROPE && s == 31) {
-                e4m3x4_to_half_cvt(rp_sel[0], rh);
-                e4m3x4_to_half_cvt(rp_sel[1], rh + 2);
-            }
-            if constexpr (ROPE && s == 32) lds_st<u32x4_t>(rq, u32x4_t{rh[0], rh[1], rh[2], rh[3]});
-            // ---- the new scores to the exchange buffer, between the dequant stores
-            if constexpr (s == 20 || s == 24 || s == 28 || s == 33) x_store(sacc, s == 33 ? 3 : (s - 20) / 4);
-            // ---- gather of tile t+4 into cur, piece by piece
-            if constexpr (s == 3) {
-                nvalid = next_slot >= 0;
-                nrow = nvalid ? p.pool + (int64_t)next_slot * kRowB : stand_in;
-            }
-            if constexpr (s == 7) {
-                cur.valid = nvalid;
-                cur.sc = *reinterpret_cast<const uint32_t *>(nrow + kScaleOff + 4 * gp);
-            }
-            if constexpr (s == 14) cur.c0 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp);
-            if constexpr (s == 30) cur.c1 = *reinterpret_cast<const u32x4_t *>(nrow + 32 * gp + 16);
-            if constexpr (ROPE && s == 32) cur.rp = *reinterpret_cast<const u32x2_t *>(nrow + kRopeOff + 8 * gp);
-            __builtin_amdgcn_sched_barrier(0);
-        });
+    // rows of tile t below this are entries, the rest padding
+    auto tile_lim = [&](int t) { return t < n_real - 1 ? kTile : t == n_real - 1 ? last_rows : 0; };
+    // a fresh chunk: translate and pack its slots (every thread, three barriers)
+    auto fresh_chunk = [&](int c_lo, int c_hi) {
+        __syncthreads();                           // slots of the previous chunk are no longer read
+        load_positions(lc, c_lo, c_hi, tid, pos);
+        load_pages(p, lc, pos, phys);
+        nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
         __syncthreads();
     };
-
-    // the first chunk's first two tiles are on their way while the queries
-    // are converted (the staged queries are read before its barrier, so the
-    // tiles may then overwrite them)
-    RowPart r0, r1;
-    {
-        const int n_t0 = (nv + kTile - 1) / kTile;
-        if (n_t0 > 0) {
-            gather_part<ROPE>(p.pool, stand_in, slots[gr], gp, r0);
-            gather_part<ROPE>(p.pool, stand_in, slots[min(1, n_t0 - 1) * kTile + gr], gp, r1);
-        }
-        convert_queries();
-    }
-
-    for (int pass = 0; pass < 2; ++pass) {
+    // one round of the output: 32 heads (staged in LDS) x 512 dims, every thread
+    auto store_round = [&](int hb) {
+        const int64_t ob = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = floatx16_t{};
-        l_run = 0.0f;
-        if (pass == 1) m_ref = m_max;              // the exact maximum: no P can exceed 1
-        for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
-            const int c_hi = min(e_hi, c_lo + kSlotCap);
-            if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) {
-                __syncthreads();                   // slots of the previous chunk are no longer read
-                load_positions(c_lo, c_hi);
-                load_pages();
-                nv = write_slots();
+        for (int i = 0; i < 8; ++i) {              // 32 heads x 128 pieces of 4 dims
+            const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
+            const int head = h0 + 32 * hb + hh;
+            if (head < p.n_heads) {
+                const floatx4_t v = lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc);
+                const int64_t off = ob + (int64_t)head * kLatent + 4 * pc;
+                if (p.out_h) *reinterpret_cast<half4_t *>(p.out_h + off) = __builtin_convertvector(v, half4_t);
+                else *reinterpret_cast<floatx4_t *>(p.out + off) = v;
+            }
+        }
+    };
+
+    if (w < 4) {
+        // ================================================ score wavefronts
+        const int hg = w & 1, half = w >> 1;
+        // parts 0..7 of a tile's rows, with the rope (for fp32 queries, whose
+        // registers these wavefronts need, the P.V wavefronts take them)
+        constexpr bool kDq = !QF32;
+        GSet<ROPE> G0, G1;
+        if (kDq && nv > 0) {                       // tile 1 exists: chunks have an even number of tiles
+            gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+            gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+        }
+
+        // queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head h0 +
+        // 32hg + l32, dims kHd half + 16 ks + 8 g .. +7 for ks < kKs.  The
+        // power-of-two scale qs puts the head's largest |q| (over all dims: the
+        // two halves agree through LDS) in [2^13, 2^14): exact in fp16 for bf16
+        // queries; fp32 queries get a hi and a lo fp16 part.  The staged
+        // fragment is read twice, for the maximum and then for the conversion,
+        // so it never occupies registers beside its fp16 form.
+        half8_t qb[kKs];
+        half8_t ql[QF32 ? kKs : 1];
+        float score_mul = 0.0f;
+        {
+            const uint32_t qf = L + (QF32 ? l32 : 32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
+            auto frag_max = [&]() {
+                float qmax = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) {
+                    if constexpr (QF32) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+                            qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                                         __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+                        }
+                    } else {
+                        const u32x4_t v = lds_ld<u32x4_t>(qf + 32 * ks);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[c] << 16)),
+                                                                         __builtin_fabsf(__uint_as_float(v[c] & 0xFFFF0000u))));
+                    }
+                }
+                qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
+                if (g == 0) red[(hg * 2 + half) * 32 + l32] = qmax;
+            };
+            auto frag_convert = [&]() {
+                const float qmax = __builtin_fmaxf(red[(hg * 2) * 32 + l32], red[(hg * 2 + 1) * 32 + l32]);
+                int ex = 0;
+                if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
+                const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
+                score_mul = p.score_mul / qs;
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) {
+                    if constexpr (QF32) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float x = v[e] * qs;
+                                const _Float16 hi = (_Float16)x;
+                                qb[ks][4 * j + e] = hi;
+                                ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
+                            }
+                        }
+                    } else {
+                        const u32x4_t v = lds_ld<u32x4_t>(qf + 32 * ks);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            qb[ks][2 * c] = (_Float16)(__uint_as_float(v[c] << 16) * qs);
+                            qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[c] & 0xFFFF0000u) * qs);
+                        }
+                    }
+                }
+            };
+            // rounds of staged queries: bf16 one, fp32 two (head group hg
+            // converts in round hg); three barriers each
+#pragma unroll 1
+            for (int round = 0; round < (QF32 ? 2 : 1); ++round) {
+                if (round > 0) {                   // the second head group's queries
+                    load_q(round, qc);
+                    stage_q(qc);
+                    __syncthreads();
+                }
+                const bool mine = !QF32 || hg == round;
+                if (mine) frag_max();
+                __syncthreads();
+                if (mine) frag_convert();
+                __syncthreads();                   // the staged queries may be overwritten
+            }
+        }
+
+        // score operand (A of S^T = K Q^T): row l32, chunk kHc half + 2 ks + g;
+        // even and odd k-steps differ in the row permutation (kHc is a
+        // multiple of 4)
+        const uint32_t sc_off0 = (kHc * half + g) * kChunkB + 16 * (l32 ^ (4 * g));
+        const uint32_t sc_off1 = (kHc * half + g) * kChunkB + 16 * (l32 ^ (4 * (g + 2)));
+        // partial scores for the partner's rows go to X[hg][1 - half], ours
+        // come from X[hg][half] (32 bytes per lane)
+        const uint32_t x_w = L + kOffX + ((hg * 2 + 1 - half) * 64 + lane) * 32;
+        const uint32_t x_r = L + kOffX + ((hg * 2 + half) * 64 + lane) * 32;
+        // P of this lane's head, rows 16 half + 8 (v / 4) + 4 g + v % 4 for v <
+        // 8, stored in the order that puts the B operand of P.V k-step kk
+        // (rows 16kk + 4g + 0..3, 16kk + 8 + 4g + 0..3) in 16 contiguous bytes
+        // (row bits 2 and 3 swapped): here 16 bytes at 16 half + 8 g
+        const uint32_t px_w = L + kOffPX + (32 * hg + l32) * kPXHead + 2 * (16 * half + 8 * g);
+
+        float m_ref = -__builtin_inff();   // reference of P = 2^(s - m_ref) for this lane's head
+        float m_max = -__builtin_inff();   // largest score this lane has seen
+        float l_run = 0.0f;                // sum of this lane's fp16 P
+        bool need_redo = false;
+        floatx4_t own0 = {0, 0, 0, 0}, own1 = {0, 0, 0, 0};   // this half's partial of its own 16 rows
+        floatx16_t sacc;
+
+        // partial S^T of the K tile at kb over this half's dims; the operand
+        // reads go out kAhead MFMAs ahead
+        auto scores = [&](uint32_t kb) {
+            const uint32_t a0 = kb + sc_off0, a1 = kb + sc_off1;
+            half8_t a[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>((i & 1 ? a1 : a0) + 2 * kChunkB * i);
+            __builtin_amdgcn_sched_barrier(0);     // keep the reads ahead of their MFMAs
+            floatx16_t acc = {};
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+                const half8_t cur = a[ks % kAhead];
+                acc = mfma32(cur, qb[ks], acc);
+                if constexpr (QF32) acc = mfma32(cur, ql[ks], acc);
+                if (ks + kAhead < kKs) {
+                    const int n = ks + kAhead;
+                    a[ks % kAhead] = lds_ld<half8_t>((n & 1 ? a1 : a0) + 2 * kChunkB * n);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            sacc = acc;
+        };
+        // the partner's 16 rows to it, ours kept (half is scalar: no lane mask)
+        auto exchange = [&]() {
+            if (half == 0) {
+                lds_st<floatx4_t>(x_w, floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]});
+                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]});
+                own0 = floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]};
+                own1 = floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]};
+            } else {
+                lds_st<floatx4_t>(x_w, floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]});
+                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]});
+                own0 = floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]};
+                own1 = floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]};
+            }
+        };
+        // scores of this lane's rows 16 half + 8 (v / 4) + 4 g + v % 4: our
+        // half's partial plus the partner's
+        auto row_raw = [&](floatx4_t x0, floatx4_t x1, float (&raw)[8]) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                raw[j] = own0[j] + x0[j];
+                raw[4 + j] = own1[j] + x1[j];
+            }
+        };
+        auto row_of = [&](int v) { return 16 * half + 8 * (v >> 2) + 4 * g + (v & 3); };
+        // P = 2^(s - m_ref) of this lane's rows to LDS; rows >= lim are padding
+        // (lim < 32 only on the chunk's last two tiles)
+        auto softmax = [&](int lim, floatx4_t x0, floatx4_t x1) {
+            float raw[8], e[8];
+            row_raw(x0, x1, raw);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+            if (lim < kTile) {                     // scalar
+#pragma unroll
+                for (int v = 0; v < 8; ++v)
+                    if (row_of(v) >= lim) e[v] = -__builtin_inff();
+            }
+            const float emax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(e[0], e[1]), __builtin_fmaxf(e[2], e[3])),
+                                               __builtin_fmaxf(__builtin_fmaxf(e[4], e[5]), __builtin_fmaxf(e[6], e[7])));
+            m_max = __builtin_fmaxf(m_max, emax + m_ref);
+            need_redo |= emax > kRefSlack;         // P could overflow fp16
+            half8_t ph;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) ph[v] = (_Float16)__builtin_amdgcn_exp2f(e[v]);   // exp2(-inf) = 0
+            const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            float ls0 = __builtin_amdgcn_fdot2(half2_t{ph[0], ph[1]}, one2, 0.0f, false);
+            float ls1 = __builtin_amdgcn_fdot2(half2_t{ph[4], ph[5]}, one2, 0.0f, false);
+            ls0 = __builtin_amdgcn_fdot2(half2_t{ph[2], ph[3]}, one2, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2(half2_t{ph[6], ph[7]}, one2, ls1, false);
+            l_run += ls0 + ls1;
+            lds_st<half8_t>(px_w, ph);
+        };
+        // Phase 1 of a tile, laid out by hand: the MFMAs of the scores of t + 1
+        // (one per slot, operands read kAhead slots ahead) with the softmax of
+        // t spread between them, so the in-order wavefront issues its VALU work
+        // while the MFMA chain runs instead of after it.
+        auto scores_softmax = [&](uint32_t kb, int lim) {
+            const floatx4_t x0 = lds_ld<floatx4_t>(x_r), x1 = lds_ld<floatx4_t>(x_r + 16);
+            const uint32_t a0 = kb + sc_off0, a1 = kb + sc_off1;
+            half8_t a[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>((i & 1 ? a1 : a0) + 2 * kChunkB * i);
+            __builtin_amdgcn_sched_barrier(0);
+            floatx16_t acc = {};
+            float raw[8], e[8], emax = 0.0f, ls0 = 0.0f, ls1 = 0.0f;
+            half8_t ph;
+            const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            static_for<0, kKs>([&](auto slot) {
+                constexpr int ks = decltype(slot)::value;
+                const half8_t cur = a[ks % kAhead];
+                acc = mfma32(cur, qb[ks], acc);
+                if constexpr (QF32) acc = mfma32(cur, ql[ks], acc);
+                if constexpr (ks + kAhead < kKs)
+                    a[ks % kAhead] = lds_ld<half8_t>(((ks + kAhead) & 1 ? a1 : a0) + 2 * kChunkB * (ks + kAhead));
+                if constexpr (ks == 2)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) raw[j] = own0[j] + x0[j];
+                if constexpr (ks == 3)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) raw[4 + j] = own1[j] + x1[j];
+                if constexpr (ks == 4)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+                if constexpr (ks == 5)
+#pragma unroll
+                    for (int v = 4; v < 8; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+                if constexpr (ks == 6) {
+                    if (lim < kTile) {             // scalar: the chunk's last two tiles only
+#pragma unroll
+                        for (int v = 0; v < 8; ++v)
+                            if (row_of(v) >= lim) e[v] = -__builtin_inff();
+                    }
+                }
+                if constexpr (ks == 7)
+                    emax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(e[0], e[1]), __builtin_fmaxf(e[2], e[3])),
+                                           __builtin_fmaxf(__builtin_fmaxf(e[4], e[5]), __builtin_fmaxf(e[6], e[7])));
+                if constexpr (ks == 8) {
+                    m_max = __builtin_fmaxf(m_max, emax + m_ref);
+                    need_redo |= emax > kRefSlack;     // P could overflow fp16
+                }
+                if constexpr (ks >= 9 && ks < 13)
+#pragma unroll
+                    for (int v = 2 * (ks - 9); v < 2 * (ks - 9) + 2; ++v) e[v] = __builtin_amdgcn_exp2f(e[v]);
+                if constexpr (ks == 13) {
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) ph[v] = (_Float16)e[v];   // exp2(-inf) = 0
+                }
+                if constexpr (ks == 14) {
+                    ls0 = __builtin_amdgcn_fdot2(half2_t{ph[0], ph[1]}, one2, 0.0f, false);
+                    ls1 = __builtin_amdgcn_fdot2(half2_t{ph[4], ph[5]}, one2, 0.0f, false);
+                    ls0 = __builtin_amdgcn_fdot2(half2_t{ph[2], ph[3]}, one2, ls0, false);
+                    ls1 = __builtin_amdgcn_fdot2(half2_t{ph[6], ph[7]}, one2, ls1, false);
+                }
+                if constexpr (ks == 15) {
+                    l_run += ls0 + ls1;
+                    lds_st<half8_t>(px_w, ph);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            sacc = acc;
+        };
+        // phase 1: softmax of t, scores of t + 1; phase 2: the swap of t + 1's
+        // partials, dequantization of t + 2 (latent dims 0..255 and the rope)
+        // and the gather of t + 4 (a tile index past the chunk is clamped to
+        // its last tile: a harmless repeat that keeps the loads unconditional)
+        auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bB, uint32_t bC) {
+            const int32_t next = slots[min(t + 4, n_t - 1) * kTile + gr];
+            if (t + 1 < n_t) scores_softmax(bB, tile_lim(t));
+            else softmax(tile_lim(t), lds_ld<floatx4_t>(x_r), lds_ld<floatx4_t>(x_r + 16));
+            __syncthreads();
+            if (t + 1 < n_t) exchange();
+            if constexpr (kDq) {
+                if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, true, G);
+                gather_set<ROPE>(p.pool, stand_in, next, gp, G);
+            }
+            __syncthreads();
+        };
+
+        for (int pass = 0; pass < 2; ++pass) {
+            l_run = 0.0f;
+            for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
+                const int c_hi = min(e_hi, c_lo + kSlotCap);
+                if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) fresh_chunk(c_lo, c_hi);
+                chunk_tiles();
+                if (n_real == 0) continue;         // nothing valid in this chunk (uniform)
+                // tiles 0 and 1 into K0 and K1, tiles 2 and 3 in flight, scores of tile 0
+                if constexpr (kDq) {
+                    if (pass == 1 || c_lo != e_lo) {   // the first chunk's were gathered before the passes
+                        gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+                        gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+                    }
+                    dequant_set<ROPE>(K0, gr, gp, true, G0);
+                    gather_set<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, G0);
+                    dequant_set<ROPE>(K1, gr, gp, true, G1);
+                    gather_set<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, G1);
+                }
+                __syncthreads();                   // tiles 0 and 1 in LDS
+                scores(K0);
+                exchange();
+                __syncthreads();
+                if (!have_ref) {                   // first tile with entries: agree on each head's reference
+                    float raw[8];
+                    row_raw(lds_ld<floatx4_t>(x_r), lds_ld<floatx4_t>(x_r + 16), raw);
+                    float tmax = -__builtin_inff();
+                    const int lim = tile_lim(0);
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+                        if (row_of(v) < lim) tmax = __builtin_fmaxf(tmax, raw[v] * score_mul);
+                    tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+                    if (g == 0) red[(hg * 2 + half) * 32 + l32] = tmax;
+                    __syncthreads();
+                    m_ref = __builtin_fmaxf(red[(hg * 2) * 32 + l32], red[(hg * 2 + 1) * 32 + l32]);
+                    have_ref = true;
+                }
+                uint32_t bA = K0, bB = K1, bC = K2;
+                for (int t = 0; t < n_t; t += 2) {
+                    iteration(t, G0, bB, bC);      // G0: tile t + 2 -> bC, then t + 4
+                    iteration(t + 1, G1, bC, bA);  // G1: tile t + 3 -> bA, then t + 5
+                    const uint32_t a0 = bA;        // tiles t + 2, t + 3, t + 4 go to bC, bA, bB
+                    bA = bC;
+                    bC = bB;
+                    bB = a0;
+                }
+            }
+            if (need_redo) *flag = 1;
+            __syncthreads();
+            if (pass == 1 || *flag == 0) break;    // uniform: read after the barrier
+            // second pass: the exact maximum of every head as its reference
+            const float mm = __builtin_fmaxf(m_max, __shfl_xor(m_max, 32));
+            if (g == 0) red[(hg * 2 + half) * 32 + l32] = mm;
+            __syncthreads();
+            m_ref = __builtin_fmaxf(red[(hg * 2) * 32 + l32], red[(hg * 2 + 1) * 32 + l32]);
+        }
+
+        if (err && p.err_word) atomicOr(p.err_word, err);
+        // row sums: the two lanes of a head, then the two halves
+        __syncthreads();
+        {
+            const float l2 = l_run + __shfl_xor(l_run, 32);
+            if (g == 0) red[(hg * 2 + half) * 32 + l32] = l2;
+        }
+        __syncthreads();
+        const float l_tot = red[(hg * 2) * 32 + l32] + red[(hg * 2 + 1) * 32 + l32];
+        const int head = h0 + 32 * hg + l32;
+        if (half == 0 && g == 0 && head < p.n_heads && p.lse) {
+            const float m_fin = have_ref ? m_ref : 0.0f;
+            const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
+            p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {           // the same two barriers per round as the P.V wavefronts
+            __syncthreads();                       // the previous round's stores are done
+            __syncthreads();                       // the P.V wavefronts have staged 32 heads
+            store_round(hb);
+        }
+    } else {
+        // ================================================ P.V wavefronts
+        const int dq = w - 4;
+#pragma unroll 1
+        for (int round = 0; round < (QF32 ? 2 : 1); ++round) {   // the score wavefronts convert the queries
+            if (round > 0) {
+                load_q(round, qc);
+                stage_q(qc);
                 __syncthreads();
             }
-            const int n_t = (nv + kTile - 1) / kTile;
-            if (n_t == 0) continue;                // nothing valid in this chunk (uniform)
-            last_rows = nv - kTile * (n_t - 1);
-            // prologue: tiles 0 and 1 into buffers 0 and 1, tiles 2 and 3 in
-            // flight in registers, scores of tile 0
-            uint32_t bA = kb0, bB = kb0 + kKTileBytes, bC = kb0 + 2 * kKTileBytes;
-            if (pass == 1 || c_lo != e_lo) {       // the first chunk's were gathered before the passes
-                gather_part<ROPE>(p.pool, stand_in, slots[gr], gp, r0);
-                gather_part<ROPE>(p.pool, stand_in, slots[min(1, n_t - 1) * kTile + gr], gp, r1);
-            }
-            dequant_part<ROPE>(pin(bA + dq_off), pin(bA + rope_off), r0);
-            gather_part<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, r0);
-            dequant_part<ROPE>(pin(bB + dq_off), pin(bB + rope_off), r1);
-            gather_part<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, r1);
-            __syncthreads();                       // tiles 0 and 1 in LDS
-            scores_to_x(pin(bA + qk_off), 0);
             __syncthreads();
-            // full tiles two at a time, then the last one or two with the
-            // last tile masked
-            int t = 0;
-            for (; t + 2 < n_t; t += 2) {
-                iteration(std::false_type{}, t, n_t, r0, bA, bB, bC, 0);       // r0: tile t+2 -> LDS, then t+4
-                iteration(std::false_type{}, t + 1, n_t, r1, bB, bC, bA, 1);   // r1: tile t+3 -> LDS, then t+5
-                const uint32_t a0 = bA;            // tiles t+2, t+3, t+4 go to bC, bA, bB
-                bA = bC;
-                bC = bB;
-                bB = a0;
-            }
-            if (t + 1 < n_t) {
-                iteration(std::false_type{}, t, n_t, r0, bA, bB, bC, 0);
-                iteration(std::true_type{}, t + 1, n_t, r1, bB, bC, bA, 1);
-            } else {
-                iteration(std::true_type{}, t, n_t, r0, bA, bB, bC, 0);
-            }
-            if (need_redo) *redo = 1;
-            __syncthreads();                       // buffers free for the next chunk or pass
+            __syncthreads();
         }
-        if (pass == 1 || *redo == 0) break;        // uniform: read after the last barrier
-    }
+        // parts 8..15 of a tile's rows, no rope; with fp32 queries also parts
+        // 0..7 with the rope (unit 1)
+        constexpr int kUnits = QF32 ? 2 : 1;
+        GSet<ROPE> G0[kUnits], G1[kUnits];
+        auto gather_units = [&](int tile, GSet<ROPE> (&G)[kUnits]) {
+            const int32_t slot = slots[tile * kTile + gr];
+            gather_set<ROPE, false>(p.pool, stand_in, slot, gp, G[0]);
+            if constexpr (kUnits == 2) gather_set<ROPE>(p.pool, stand_in, slot, gp - 8, G[1]);
+        };
+        auto dequant_units = [&](uint32_t kb, const GSet<ROPE> (&G)[kUnits]) {
+            dequant_set<ROPE>(kb, gr, gp, false, G[0]);
+            if constexpr (kUnits == 2) dequant_set<ROPE>(kb, gr, gp - 8, true, G[1]);
+        };
+        if (nv > 0) {
+            gather_units(0, G0);
+            gather_units(1, G1);
+        }
+        // transposing reads (A of O^T = V^T P^T): this lane names row j4 + 4g
+        // (+8 for the second read of a k-step, +16 for the second k-step), 8
+        // bytes at latent dims 128 dq + 32 md + 8 cc + 4 (lane & 1) .. +3, so
+        // each lane receives a column of a row-major 4 x 16 block
+        const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), j4 = (lane >> 2) & 3;
+        const uint32_t tr_off0 = (16 * dq + cc) * kChunkB + 16 * (j4 + 4 * (g ^ (cc & 1)) + 8 * (cc >> 1)) + 8 * (lane & 1);
+        const uint32_t tr_off1 = (16 * dq + cc) * kChunkB + 16 * (j4 + 4 * (g ^ (cc & 1)) + 8 * (1 ^ (cc >> 1))) + 8 * (lane & 1);
+        // B operand of k-step kk for heads 32 hb .. +31: head l32, P rows at 16kk + 8g
+        const uint32_t px_r = L + kOffPX + l32 * kPXHead + 2 * (8 * g);
+        floatx16_t o[4][2];                        // [dims block md][head block hb]
 
-    if (err && p.err_word) atomicOr(p.err_word, err);
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float m_fin = m_ref == -__builtin_inff() ? 0.0f : m_ref;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    // O^T of this wavefront (256 dims x 32 heads) leaves through LDS, free
-    // since the passes' last barrier: stored straight from the accumulators
-    // every store instruction would touch 32 heads' rows 2 KB apart; from LDS
-    // each one writes 1 KB of one head's row.  Wavefront w's region holds
-    // [32 heads][256 dims + 4 pad] floats (the padding keeps the transposed
-    // writes conflict-free).
-    constexpr int kORow = 256 + 4;
-    const uint32_t oreg = kb0 + wave * (32 * kORow * 4);
-    static_assert(4 * 32 * kORow * 4 <= kSlotOff - 16, "output staging overlaps the slot list");
-    {
-        const uint32_t ow = pin(oreg + (l32 * kORow + 4 * g) * 4);
+        // O^T += V^T P^T for the K tile at kb, both head blocks sharing each V^T
+        // operand; the transposing reads go out kTrAhead MFMA pairs ahead
+        auto pv = [&](uint32_t kb) {
+            const uint32_t t0 = kb + tr_off0, t1 = kb + tr_off1;
+            half8_t pb[2][2];
 #pragma unroll
-        for (int md = 0; md < 8; ++md)
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                lds_st<floatx4_t>(ow + (32 * md + 8 * j) * 4,
-                                  floatx4_t{o[md][4 * j], o[md][4 * j + 1], o[md][4 * j + 2], o[md][4 * j + 3]} * inv);
-    }
-    __syncthreads();
-    {
-        const uint32_t orr = pin(oreg + 16 * lane);
-        const int64_t ob = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + 256 * half + 4 * lane;
-        if (p.out_h) {                             // fp16 split partials (|o| <= 2688): half the bytes to store
+                for (int kk = 0; kk < 2; ++kk) pb[hb][kk] = lds_ld<half8_t>(px_r + hb * (32 * kPXHead) + 32 * kk);
+            short4_t lo[kTrAhead], hi[kTrAhead];
+            auto issue = [&](int j) {              // pair j: k-step kk = j / 4, dims block md = j % 4
+                const int md = j & 3, kk = j >> 2;
+                lo[j % kTrAhead] = lds_read_tr16(t0 + 4 * kChunkB * md + 256 * kk);
+                hi[j % kTrAhead] = lds_read_tr16(t1 + 4 * kChunkB * md + 256 * kk);
+            };
 #pragma unroll
-            for (int h = 0; h < 32; ++h) {
-                const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
-                if (hg * 32 + h < p.n_heads)
-                    *reinterpret_cast<half4_t *>(p.out_h + ob + (int64_t)(hg * 32 + h) * kLatent) =
-                        __builtin_convertvector(v, half4_t);
+            for (int j = 0; j < kTrAhead; ++j) issue(j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int md = j & 3, kk = j >> 2;
+                const half8_t a = __builtin_bit_cast(
+                    half8_t, __builtin_shufflevector(lo[j % kTrAhead], hi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+                o[md][0] = mfma32(a, pb[0][kk], o[md][0]);
+                o[md][1] = mfma32(a, pb[1][kk], o[md][1]);
+                if (j + kTrAhead < 8) issue(j + kTrAhead);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        } else {
+        };
+        // phase 1: dequantization of t + 2 (latent dims 256..511) and the
+        // gather of t + 4; phase 2: P.V of t
+        auto iteration = [&](int t, GSet<ROPE> (&G)[kUnits], uint32_t bA, uint32_t bC) {
+            if (t + 2 < n_t) dequant_units(bC, G);
+            gather_units(min(t + 4, n_t - 1), G);
+            __syncthreads();
+            pv(bA);
+            __syncthreads();
+        };
+
+        for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-            for (int h = 0; h < 32; ++h) {
-                const floatx4_t v = lds_ld<floatx4_t>(orr + h * kORow * 4);
-                if (hg * 32 + h < p.n_heads)
-                    *reinterpret_cast<floatx4_t *>(p.out + ob + (int64_t)(hg * 32 + h) * kLatent) = v;
+            for (int md = 0; md < 4; ++md) o[md][0] = o[md][1] = floatx16_t{};
+            for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
+                const int c_hi = min(e_hi, c_lo + kSlotCap);
+                if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) fresh_chunk(c_lo, c_hi);
+                chunk_tiles();
+                if (n_real == 0) continue;
+                if (pass == 1 || c_lo != e_lo) {
+                    gather_units(0, G0);
+                    gather_units(1, G1);
+                }
+                dequant_units(K0, G0);
+                gather_units(min(2, n_t - 1), G0);
+                dequant_units(K1, G1);
+                gather_units(min(3, n_t - 1), G1);
+                __syncthreads();                   // tiles 0 and 1 in LDS
+                __syncthreads();                   // the score wavefronts' tile-0 partials are swapped
+                if (!have_ref) {
+                    __syncthreads();               // the reference is agreed
+                    have_ref = true;
+                }
+                uint32_t bA = K0, bB = K1, bC = K2;
+                for (int t = 0; t < n_t; t += 2) {
+                    iteration(t, G0, bA, bC);
+                    iteration(t + 1, G1, bB, bA);
+                    const uint32_t a0 = bA;
+                    bA = bC;
+                    bC = bB;
+                    bB = a0;
+                }
             }
+            __syncthreads();
+            if (pass == 1 || *flag == 0) break;
+            __syncthreads();                       // the second pass's reference is agreed
         }
-    }
-    if (head_live && half == 0 && g == 0 && p.lse) {
-        const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
-        p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
+
+        if (err && p.err_word) atomicOr(p.err_word, err);
+        __syncthreads();
+        __syncthreads();                           // the row sums are in red[]
+        const uint32_t ow = L + l32 * (kORow * 4) + 4 * (128 * dq + 4 * g);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const float l_tot = red[(hb * 2) * 32 + l32] + red[(hb * 2 + 1) * 32 + l32];
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            __syncthreads();                       // the previous round's stores have read the staging area
+#pragma unroll
+            for (int md = 0; md < 4; ++md)
+#pragma unroll
+                for (int vq = 0; vq < 4; ++vq)
+                    lds_st<floatx4_t>(ow + 4 * (32 * md + 8 * vq),
+                                      floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
+                                                o[md][hb][4 * vq + 3]} * inv);
+            __syncthreads();
+            store_round(hb);
+        }
     }
 }
 
@@ -718,82 +873,71 @@ hipError_t launch_sparse_mla(const AttnParams &p, bool q_f32, int32_t n_splits, 
     if (p.n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)p.n_rows, (unsigned)n_splits, (unsigned)((p.n_heads + 63) / 64));
     if (p.rope_dims == kRope) {
-        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid, dim3(256), 0, stream, p);
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
     } else {
-        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid, dim3(256), 0, stream, p);
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
 
 // --------------------------------------------------- dequantizing gather
 
-// One workgroup per (query row, tile of 32 entries): translate, then the same
-// lane roles and decoding as the attention kernel, written row-major to HBM
-// (576 fp16 values per entry, or 512 for rope-free rows).
-__global__ __launch_bounds__(256) void gather_dequant_kernel(AttnParams p, uint16_t *__restrict__ out,
-                                                             int32_t *__restrict__ slots_out) {
-    __shared__ int32_t slots[kTile];
-    const int tid = threadIdx.x, r = blockIdx.x, tile = blockIdx.y;
-    const int32_t req = p.row_req ? p.row_req[r] : r;
-    const bool bad_req = p.page_table && (req < 0 || req >= p.pt_n_rows);
-    const int32_t *pt_row = p.page_table && !bad_req ? p.page_table + (int64_t)req * p.pt_row_stride : nullptr;
+// A test and debugging aid that runs the attention kernel's own front end:
+// one workgroup per (query row, chunk of 2048 entries) translates the chunk
+// with load_positions / load_pages / pack_slots and dequantizes each tile with
+// gather_set / dequant_set into an LDS K tile, which it then copies out
+// row-major.  Entry j of a chunk's output is the j-th valid entry of the chunk
+// (list order), as the attention kernel's tiles hold it; entries past the valid
+// count get slot -1 and zeros.
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void gather_dequant_kernel(AttnParams p, uint16_t *__restrict__ out,
+                                                                  int32_t *__restrict__ slots_out) {
+    constexpr int kD = ROPE ? kDim : kLatent;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kKTileB + kSlotCap * 4 + kPosPerLane * 8 * 4];
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + kKTileB);
+    int32_t *counts = reinterpret_cast<int32_t *>(lds + kKTileB + kSlotCap * 4);
+    const uint32_t kb = lds_addr(lds);
+    const int tid = threadIdx.x, gr = tid & 31, gp = tid >> 5;
+    const int r = blockIdx.x;
+    const int c_lo = blockIdx.y * kSlotCap, c_hi = min(p.k, c_lo + kSlotCap);
+    const ListCtx lc = list_ctx(p, r);
     uint32_t err = 0;
-    if (tid < kTile) {
-        const int e = tile * kTile + tid;
-        int64_t s = -1;
-        if (e < p.k) {
-            const int32_t pos = p.topk[(int64_t)r * p.topk_row_stride + e];
-            if (bad_req) err |= pos >= 0 ? kErrPage : 0u;
-            else s = translate_slot(pos, pt_row, p.pt_n_pages, p.page_shift, p.n_slots, err);
-            if (slots_out) slots_out[(int64_t)r * p.k + e] = (int32_t)s;
-        }
-        slots[tid] = (int32_t)s;
-        if (err && p.err_word) atomicOr(p.err_word, err);
-    }
+    int32_t pos[kPosPerLane], phys[kPosPerLane];
+    load_positions(lc, c_lo, c_hi, tid, pos);
+    load_pages(p, lc, pos, phys);
+    const int nv = pack_slots(p, lc, pos, phys, tid, slots, counts, err);
     __syncthreads();
-    const bool rope = p.rope_dims == kRope;
-    const int row_b = rope ? kRowBytes : kScaleOff + kLatent / 16, dim = rope ? kDim : kLatent;
-    const int pp = tid & 15, qc = tid >> 4;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = 2 * pp + h, e = tile * kTile + row;
-        if (e >= p.k) continue;
-        const int32_t s = slots[row];
-        u32x4_t codes = {0, 0, 0, 0};
-        uint32_t sc = 0;
-        if (s >= 0) {
-            const uint8_t *src = p.pool + (int64_t)s * row_b;
-            codes = *reinterpret_cast<const u32x4_t *>(src + 16 * qc);
-            sc = *reinterpret_cast<const uint16_t *>(src + kScaleOff + 2 * qc);
+    if (err && p.err_word) atomicOr(p.err_word, err);
+    const int64_t base = (int64_t)r * p.k + c_lo;
+    if (slots_out)
+        for (int e = tid; e < c_hi - c_lo; e += kThreads) slots_out[base + e] = e < nv ? slots[e] : -1;
+    const int n_t = (nv + kTile - 1) / kTile;
+    const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(out);   // any 352 readable bytes: the output (>= 1024)
+    for (int t = 0; t * kTile < c_hi - c_lo; ++t) {
+        if (t < n_t) {
+            GSet<ROPE> G;
+            gather_set<ROPE>(p.pool, stand_in, slots[t * kTile + gr], gp, G);
+            dequant_set<ROPE>(kb, gr, gp, tid < 256, G);
         }
-        uint32_t v[16];
-        dequant_chunk(codes, sc, v);
-        uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * dim) + 16 * qc;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<u32x4_t *>(dst + 4 * c) = u32x4_t{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
-    }
-    if (rope && tid < 128) {
-        const int row = tid >> 2, e = tile * kTile + row;
-        if (e < p.k) {
-            const int32_t s = slots[row];
-            u32x4_t b = {0, 0, 0, 0};
-            if (s >= 0) b = *reinterpret_cast<const u32x4_t *>(p.pool + (int64_t)s * kRowBytes + kRopeOff + 16 * (tid & 3));
-            uint32_t h[8];
-            dequant_rope16(b, h);
-            uint32_t *dst = reinterpret_cast<uint32_t *>(out + ((int64_t)r * p.k + e) * dim) + kLatent / 2 + 8 * (tid & 3);
-            *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{h[0], h[1], h[2], h[3]};
-            *reinterpret_cast<u32x4_t *>(dst + 4) = u32x4_t{h[4], h[5], h[6], h[7]};
+        __syncthreads();
+        for (int i = tid; i < kTile * (kD / 8); i += kThreads) {       // (row, chunk) pieces of 16 bytes
+            const int row = i / (kD / 8), c = i % (kD / 8), e = t * kTile + row;
+            if (e < c_hi - c_lo) {
+                const u32x4_t v = t < n_t ? lds_ld<u32x4_t>(kb + kswz(row, c)) : u32x4_t{0, 0, 0, 0};
+                *reinterpret_cast<u32x4_t *>(out + (base + e) * kD + 8 * c) = v;
+            }
         }
+        __syncthreads();
     }
 }
 
 hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *slots_out, hipStream_t stream) {
     if (p.n_rows == 0 || p.k == 0) return hipSuccess;
-    const dim3 grid((unsigned)p.n_rows, (unsigned)((p.k + kTile - 1) / kTile));
-    hipLaunchKernelGGL(gather_dequant_kernel, grid, dim3(256), 0, stream, p, out, slots_out);
+    const dim3 grid((unsigned)p.n_rows, (unsigned)((p.k + kSlotCap - 1) / kSlotCap));
+    if (p.rope_dims == kRope) hipLaunchKernelGGL(gather_dequant_kernel<true>, grid, dim3(kThreads), 0, stream, p, out, slots_out);
+    else hipLaunchKernelGGL(gather_dequant_kernel<false>, grid, dim3(kThreads), 0, stream, p, out, slots_out);
     return hipGetLastError();
 }
 

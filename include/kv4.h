@@ -195,7 +195,8 @@ typedef struct kv4_attn_args {
     int32_t n_rows;            /* query rows (decode: one per request) */
     int32_t n_heads;           /* multiple of 16, 16..128 */
     const uint8_t *pool;       /* device [n_slots, 352 or 288 (rope-free)]; 16-byte aligned */
-    int64_t n_slots;
+    int64_t n_slots;           /* 0 <= n_slots <= 2^31 - 1 (slots are 32-bit inside the
+                                  kernels): larger gives KV4_ERR_UNSUPPORTED */
     const int32_t *page_table; /* device, nullable: NULL => list entries are slots */
     int64_t pt_row_stride;     /* elements between page-table rows (0 = shared row) */
     int32_t pt_n_rows;         /* page-table rows; a query row whose request is outside
@@ -206,7 +207,9 @@ typedef struct kv4_attn_args {
     const int32_t *topk;       /* device [n_rows, >= k] */
     int64_t topk_row_stride;   /* elements, >= k */
     int32_t k;                 /* list length, 0 <= k <= KV4_MAX_K */
-    float sm_scale;            /* softmax scale, e.g. 1/sqrt(576) */
+    float sm_scale;            /* softmax scale, e.g. 1/sqrt(576); any finite value (a
+                                  negative one reverses the order of the scores), NaN or
+                                  infinity gives KV4_ERR_SHAPE */
     float *out;                /* device [n_rows, n_heads, 512] fp32; 16-byte aligned */
     int64_t out_row_stride;    /* elements, >= n_heads * 512, multiple of 4 */
     float *lse;                /* device [n_rows, n_heads] fp32, nullable */

@@ -86,6 +86,11 @@ BAD_ARGS = [
     (dict(page_table=0x5000, pt_n_rows=1), 2, "pt_n_rows"),
     (dict(out=0x4004), 3, "out"),
     (dict(out_row_stride=100), 3, "out_row_stride"),
+    (dict(n_slots=1 << 31), 4, "n_slots"),           # slots are 32-bit inside the kernels
+    (dict(n_slots=(1 << 31) + 5), 4, "n_slots"),
+    (dict(sm_scale=float("nan")), 2, "sm_scale"),
+    (dict(sm_scale=float("inf")), 2, "sm_scale"),
+    (dict(sm_scale=float("-inf")), 2, "sm_scale"),
 ]
 
 

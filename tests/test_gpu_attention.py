@@ -317,3 +317,59 @@ def test_rising_scores_take_the_exact_second_pass(num_splits):
     order = np.argsort(np.log(probs[:, 0, :] + 1e-300), axis=1)          # head 0's scores, ascending
     rising = np.take_along_axis(topk, order, axis=1).astype(np.int32)
     _run(spec, q, rising, pt, num_splits=num_splits)
+
+
+def _rising_lists(spec, q, pool_h, topk, pt):
+    """The lists reordered by head 0's score, ascending, and the largest log2
+    gap (over rows) between head 0's best score in the first 32 entries and its
+    best score in the whole list."""
+    _, _, _, probs = oracle.sparse_mla(q_for_oracle(q), pool_h, topk, spec.sm_scale, page_table=pt, want_probs=True)
+    order = np.argsort(np.log(probs[:, 0, :] + 1e-300), axis=1)
+    rising = np.take_along_axis(topk, order, axis=1).astype(np.int32)
+    p = np.take_along_axis(probs[:, 0, :], order, axis=1)
+    gap = np.log2(p.max(axis=1) / p[:, :32].max(axis=1))
+    return rising, float(gap.max())
+
+
+@pytest.mark.parametrize("mode", ["decode_one_split", "prefill"])
+def test_rising_scores_redo_across_chunks(mode):
+    """Lists of 4096 entries (two translation chunks of 2048) ordered by rising
+    score: head 0's best score lies more than 16 (log2) above the first tile's,
+    so P against the first tile's reference would overflow fp16 (max 65504 <
+    2^16) and the output would be inf/NaN.  Matching the oracle therefore
+    shows the exact second pass ran, re-translating the first chunk."""
+    spec = W.scaled(SMALL, ctx=8192, n_pool_pages=160 * 4 + 8, k=4096, seed=7300)
+    pool_d, pool_h = pools(spec)
+    q = (W.queries(spec).float() * 40.0).to(torch.bfloat16)
+    topk, pt = W.topk_lists(spec), W.page_table(spec)
+    rising, gap = _rising_lists(spec, q, pool_h, topk, pt)
+    assert gap > 16.0, "the case does not force the second pass (gap %.1f)" % gap
+    if mode == "prefill":
+        _run(spec, q, rising, pt, prefill=True, row_req=np.arange(spec.n_req, dtype=np.int32),
+             pool_pair=(pool_d, pool_h))
+    else:
+        _run(spec, q, rising, pt, num_splits=1, pool_pair=(pool_d, pool_h))
+
+
+def test_rising_scores_force_the_second_pass_within_a_chunk():
+    """k = 2048 in one chunk, decode with one split and with the automatic
+    split count; the same overflow argument as above."""
+    spec = W.scaled(SMALL, ctx=8192, n_pool_pages=160 * 4 + 8, k=2048, seed=7400)
+    pool_d, pool_h = pools(spec)
+    q = (W.queries(spec).float() * 40.0).to(torch.bfloat16)
+    topk, pt = W.topk_lists(spec), W.page_table(spec)
+    rising, gap = _rising_lists(spec, q, pool_h, topk, pt)
+    assert gap > 16.0, "the case does not force the second pass (gap %.1f)" % gap
+    _run(spec, q, rising, pt, num_splits=1, pool_pair=(pool_d, pool_h))
+    _run(spec, q, rising, pt, num_splits=0, pool_pair=(pool_d, pool_h))
+
+
+@pytest.mark.parametrize("sm_scale", [-1.0 / 24.0, 0.0, 3.0])
+def test_softmax_scale_of_any_sign(sm_scale):
+    """The softmax scale is any finite number: negative scales reverse the
+    order of the scores (the reference comes from the scaled scores, not the
+    raw ones), zero makes every weight equal."""
+    spec = W.scaled(SMALL, k=300, seed=7500, softmax_scale=sm_scale)
+    q, topk, pt = W.queries(spec), W.topk_lists(spec), W.page_table(spec)
+    _run(spec, q, topk, pt, num_splits=0)
+    _run(spec, q, topk, pt, prefill=True, row_req=np.arange(spec.n_req, dtype=np.int32))

@@ -15,6 +15,7 @@ Seeds: 1000 * config number + stream id.
 from __future__ import annotations
 
 import dataclasses
+from typing import Optional
 import math
 
 import numpy as np
@@ -40,6 +41,7 @@ class DecodeSpec:
     n_query_rows: int = 0  # prefill: query rows (all in request 0); 0 = one row per request
     first_query_pos: int = 0
     seed: int = 0
+    softmax_scale: Optional[float] = None   # None: 1/sqrt(576)
 
     @property
     def n_slots(self) -> int:
@@ -55,6 +57,8 @@ class DecodeSpec:
 
     @property
     def sm_scale(self) -> float:
+        if self.softmax_scale is not None:
+            return float(np.float32(self.softmax_scale))
         return float(np.float32(1.0 / math.sqrt(DIM)))
 
 
