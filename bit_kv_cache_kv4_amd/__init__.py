@@ -23,7 +23,8 @@ __all__ = [
     "Kv4Error", "ROW_BYTES", "ROW_BYTES_ROPE_FREE", "LATENT", "ROPE", "DIM", "ERRBIT_PAGE", "ERRBIT_SLOT",
     "library_path", "load", "version", "last_error",
     "quant_write", "quant_write_mse", "dedup_compact", "write_and_dedup", "global_compact",
-    "global_compact_workspace", "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_splits",
+    "global_compact_workspace", "sparse_mla_decode", "sparse_mla_decode_noalloc", "noalloc_scratch_bytes",
+    "sparse_mla_decode_partial", "sparse_mla_decode_splits",
     "sparse_mla_decode_workspace", "merge_states", "sparse_mla_prefill", "gather_dequant",
 ]
 
@@ -95,6 +96,8 @@ def load():
     L.kv4_sparse_mla_decode_splits.argtypes, L.kv4_sparse_mla_decode_splits.restype = [pa], i32
     L.kv4_sparse_mla_decode_workspace.argtypes, L.kv4_sparse_mla_decode_workspace.restype = [pa, i32], sz
     L.kv4_sparse_mla_decode.argtypes = [pa, i32, vp, sz, vp]
+    L.kv4_sparse_mla_decode_noalloc.argtypes = [pa, i32, vp]
+    L.kv4_noalloc_scratch_bytes.argtypes, L.kv4_noalloc_scratch_bytes.restype = [], sz
     L.kv4_sparse_mla_decode_partial.argtypes = [pa, i32, vp, vp, vp]
     L.kv4_sparse_mla_decode_partial_f16.argtypes = [pa, i32, vp, vp, vp]
     L.kv4_merge_states.argtypes = [vp, vp, i32, i64, i32, vp, i64, vp, vp]
@@ -103,7 +106,7 @@ def load():
     L.kv4_gather_dequant.argtypes = [pa, vp, vp, vp]
     for f in ("kv4_quant_write", "kv4_dedup_compact", "kv4_sparse_mla_decode", "kv4_sparse_mla_decode_partial",
               "kv4_sparse_mla_decode_partial_f16", "kv4_merge_states", "kv4_merge_states_f16",
-              "kv4_sparse_mla_prefill", "kv4_gather_dequant"):
+              "kv4_sparse_mla_prefill", "kv4_gather_dequant", "kv4_sparse_mla_decode_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     if L.kv4_attn_args_size() != ctypes.sizeof(AttnArgs):
         raise Kv4Error(2, "kv4_attn_args layout mismatch: library %d bytes, binding %d"
@@ -330,6 +333,21 @@ def sparse_mla_decode(q, pool, topk, sm_scale, page_table=None, row_req=None, pa
     _check(L.kv4_sparse_mla_decode(ctypes.byref(a), int(num_splits), _ptr(workspace),
                                    0 if workspace is None else workspace.numel(), _stream(stream, q.device)))
     return out, lse
+
+
+def sparse_mla_decode_noalloc(q, pool, topk, sm_scale, page_table=None, row_req=None, page_size=64, out=None,
+                              lse=None, err_word=None, num_splits=0, stream=None):
+    """kv4_sparse_mla_decode_noalloc: decode with the split parts in the library's own scratch array
+    (no workspace; out / lse are allocated here only when not given)."""
+    out, lse = _alloc_out(q, out, lse)
+    a = _attn_args(q, pool, topk, sm_scale, page_table, row_req, page_size, out, lse, err_word)
+    _check(load().kv4_sparse_mla_decode_noalloc(ctypes.byref(a), int(num_splits), _stream(stream, q.device)))
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    """kv4_noalloc_scratch_bytes."""
+    return int(load().kv4_noalloc_scratch_bytes())
 
 
 def sparse_mla_decode_partial(q, pool, topk, sm_scale, num_splits, page_table=None, row_req=None, page_size=64,

@@ -27,6 +27,20 @@ kv4_status ok() {
     return KV4_OK;
 }
 
+}  // namespace
+
+namespace kv4 {
+kv4_status api_fail(kv4_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+}  // namespace kv4
+
+namespace {
+
 kv4_status hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(KV4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();

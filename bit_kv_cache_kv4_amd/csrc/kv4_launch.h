@@ -5,9 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kv4.h"
 #include "kv4_attn.h"
 
 namespace kv4 {
+
+// Sets kv4_last_error()'s text (printf-style) and returns st.
+kv4_status api_fail(kv4_status st, const char *fmt, ...);
 
 hipError_t launch_quant_write(const float *kv, int64_t kv_row_stride, const int32_t *slots,
                               int64_t n_tokens, uint8_t *pool, int64_t n_slots, uint32_t *err_word,

@@ -247,6 +247,28 @@ kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, voi
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * kv4_sparse_mla_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result, with the split parts held in a
+ * scratch array the library keeps on each device it runs on (allocated with
+ * the library's code, held until the process ends) instead of a workspace
+ * argument.  No allocation happens in the call.
+ *   Limit: kv4_sparse_mla_decode_workspace(a, num_splits) must not exceed
+ *   kv4_noalloc_scratch_bytes() (32 MiB); larger gives KV4_ERR_WORKSPACE with
+ *   nothing enqueued.
+ *   Every call on one device shares that device's array: calls that overlap
+ *   on one device (different streams, or one still running on the GPU while
+ *   another is enqueued on another stream) race.  Calls on one stream are
+ *   ordered and safe.
+ * Errors: those of kv4_sparse_mla_decode; KV4_ERR_HIP if the array's device
+ * address cannot be found.
+ */
+kv4_status kv4_sparse_mla_decode_noalloc(const kv4_attn_args *a, int32_t num_splits, void *stream);
+
+/* Bytes of the scratch array kv4_sparse_mla_decode_noalloc uses on each device. */
+size_t kv4_noalloc_scratch_bytes(void);
+
+/*
  * The first half of kv4_sparse_mla_decode: for each split s in
  * [0, num_splits) (num_splits >= 1), the normalised state of row r, head h
  * over the entries [s * c, min(k, (s + 1) * c)) with c = 32 * ceil(ceil(k / 32)
