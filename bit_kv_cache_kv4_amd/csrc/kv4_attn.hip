@@ -72,15 +72,16 @@ constexpr int kSlotCap = 2048;                         // entries translated per
 constexpr int kPosPerLane = kSlotCap / kThreads;
 constexpr int kOffX = kNBuf * kKTileB;                 // 110592
 constexpr int kOffPX = kOffX + kXB;                    // 118784
-constexpr int kOffSlots = kOffPX + kPXB;               // 123904
-constexpr int kOffCounts = kOffSlots + kSlotCap * 4;   // 132096
+constexpr int kStageBytes = 64 * (kDim * 4 + 16);      // 148480: all 64 fp32 query rows (K tiles, X, P and spare)
+constexpr int kOffSlots = kStageBytes;                 // 148480
+constexpr int kOffCounts = kOffSlots + kSlotCap * 4;   // 156672
 constexpr int kOffRed = kOffCounts + kPosPerLane * 8 * 4;
 constexpr int kOffFlag = kOffRed + 2 * 2 * 32 * 4;
-constexpr int kLdsBytes = kOffFlag + 16;               // 132752
-constexpr int kStageBytes = kOffX;                     // the K tiles: staging of queries and outputs
+constexpr int kLdsBytes = kOffFlag + 16;               // 157328
+static_assert(kOffPX + kPXB <= kStageBytes, "P overlaps the slot list");
 constexpr int kORow = kLatent + 4;                     // staged output row (floats; the pad spreads banks)
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
-static_assert(32 * kORow * 4 <= kStageBytes, "output staging overlaps the exchange");
+static_assert(32 * kORow * 4 <= kOffX, "output staging overlaps the exchange");
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -305,39 +306,42 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     // take consecutive 16-byte chunks of a head's row), the page-table entries
     // once the list is back, the queries staged in LDS (the K tiles are not in
     // use yet; rows padded so the fragment reads are conflict-free), the slots.
-    // bf16 queries are staged at once; fp32 ones in two rounds, one per head
-    // group.
+    // All 64 head rows are staged at once (fp32 ones fill most of the LDS;
+    // nothing else lives in it yet but the slot list, which lies beyond).
     constexpr int kQE = QF32 ? 4 : 2;                      // bytes per query element
     constexpr int kQRow = kD * kQE + 16;                   // staged head row
-    constexpr int kQH = QF32 ? 32 : 64;                    // heads staged per round
+    constexpr int kQH = 64;                                // heads staged
     constexpr int kQChunks = kD * kQE / 16;                // 16-byte chunks per head row
     constexpr int kQPer = kQH * kQChunks / kThreads;       // chunks per thread
     static_assert(kQH * kQChunks % kThreads == 0, "query chunks do not divide");
-    static_assert(kQH * kQRow <= kStageBytes, "staged queries overlap the exchange");
+    static_assert(kQH * kQRow <= kStageBytes, "staged queries overlap the slot list");
+    // thread t loads head t / kTPH, 16-byte chunks t % kTPH +
+    // kTPH i: one base address per thread, consecutive threads on consecutive
+    // chunks of a head row
+    constexpr int kTPH = kThreads / kQH;                   // threads per head row
+    static_assert(kQChunks == kTPH * kQPer, "query chunks do not divide");
     const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * kQE;
-    auto load_q = [&](int round, u32x4_t (&qc)[kQPer]) {
+    const int q_hh = tid / kTPH, q_part = tid % kTPH;
+    auto load_q = [&](u32x4_t (&qc)[kQPer]) {
+        const int head = h0 + q_hh;
+        const uint8_t *src = qr + (int64_t)min(head, p.n_heads - 1) * p.q_head_stride * kQE + 16 * q_part;
 #pragma unroll
         for (int i = 0; i < kQPer; ++i) {
-            const int c = tid + kThreads * i, hh = c / kQChunks, part = c % kQChunks;
-            const int head = h0 + kQH * round + hh;
-            qc[i] = u32x4_t{0, 0, 0, 0};
-            if (head < p.n_heads)
-                qc[i] = *reinterpret_cast<const u32x4_t *>(qr + (int64_t)head * p.q_head_stride * kQE + 16 * part);
+            qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
+            if (head >= p.n_heads) qc[i] = u32x4_t{0, 0, 0, 0};
         }
     };
     auto stage_q = [&](const u32x4_t (&qc)[kQPer]) {
+        const uint32_t dst = L + q_hh * kQRow + 16 * q_part;
 #pragma unroll
-        for (int i = 0; i < kQPer; ++i) {
-            const int c = tid + kThreads * i, hh = c / kQChunks, part = c % kQChunks;
-            lds_st<u32x4_t>(L + hh * kQRow + 16 * part, qc[i]);
-        }
+        for (int i = 0; i < kQPer; ++i) lds_st<u32x4_t>(dst + 16 * kTPH * i, qc[i]);
     };
 
     int32_t pos[kPosPerLane], phys[kPosPerLane];
     const int first_hi = min(e_hi, e_lo + kSlotCap);
     load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);   // issued first: loads complete in order
     u32x4_t qc[kQPer];
-    load_q(0, qc);
+    load_q(qc);
     load_pages(p, lc, pos, phys);
     stage_q(qc);
     int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
@@ -363,18 +367,29 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
         __syncthreads();
     };
-    // one round of the output: 32 heads (staged in LDS) x 512 dims, every thread
+    // one round of the output: 32 heads (staged in LDS) x 512 dims, every
+    // thread; one scalar base per round and 32-bit offsets per piece
     auto store_round = [&](int hb) {
-        const int64_t ob = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride;
+        const int hb0 = h0 + 32 * hb;
+        const int n_live = min(32, p.n_heads - hb0);                  // heads of this round that exist
+        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)hb0 * kLatent;
+        if (p.out_h) {
+            _Float16 *ob = p.out_h + base;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {              // 32 heads x 128 pieces of 4 dims
-            const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
-            const int head = h0 + 32 * hb + hh;
-            if (head < p.n_heads) {
-                const floatx4_t v = lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc);
-                const int64_t off = ob + (int64_t)head * kLatent + 4 * pc;
-                if (p.out_h) *reinterpret_cast<half4_t *>(p.out_h + off) = __builtin_convertvector(v, half4_t);
-                else *reinterpret_cast<floatx4_t *>(p.out + off) = v;
+            for (int i = 0; i < 8; ++i) {          // 32 heads x 128 pieces of 4 dims
+                const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
+                if (hh < n_live)
+                    *reinterpret_cast<half4_t *>(ob + (hh * kLatent + 4 * pc)) =
+                        __builtin_convertvector(lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc), half4_t);
+            }
+        } else {
+            float *ob = p.out + base;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
+                if (hh < n_live)
+                    *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pc)) =
+                        lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc);
             }
         }
     };
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         half8_t ql[QF32 ? kKs : 1];
         float score_mul = 0.0f;
         {
-            const uint32_t qf = L + (QF32 ? l32 : 32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
+            const uint32_t qf = L + (32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
             auto frag_max = [&]() {
                 float qmax = 0.0f;
 #pragma unroll
@@ -455,21 +470,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                     }
                 }
             };
-            // rounds of staged queries: bf16 one, fp32 two (head group hg
-            // converts in round hg); three barriers each
-#pragma unroll 1
-            for (int round = 0; round < (QF32 ? 2 : 1); ++round) {
-                if (round > 0) {                   // the second head group's queries
-                    load_q(round, qc);
-                    stage_q(qc);
-                    __syncthreads();
-                }
-                const bool mine = !QF32 || hg == round;
-                if (mine) frag_max();
-                __syncthreads();
-                if (mine) frag_convert();
-                __syncthreads();                   // the staged queries may be overwritten
-            }
+            frag_max();
+            __syncthreads();
+            frag_convert();
+            __syncthreads();                       // the staged queries may be overwritten
         }
 
         // score operand (A of S^T = K Q^T): row l32, chunk kHc half + 2 ks + g;
@@ -733,16 +737,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     } else {
         // ================================================ P.V wavefronts
         const int dq = w - 4;
-#pragma unroll 1
-        for (int round = 0; round < (QF32 ? 2 : 1); ++round) {   // the score wavefronts convert the queries
-            if (round > 0) {
-                load_q(round, qc);
-                stage_q(qc);
-                __syncthreads();
-            }
-            __syncthreads();
-            __syncthreads();
-        }
+        __syncthreads();                           // the score wavefronts convert the queries
+        __syncthreads();
         // parts 8..15 of a tile's rows, no rope; with fp32 queries also parts
         // 0..7 with the rope (unit 1)
         constexpr int kUnits = QF32 ? 2 : 1;
