@@ -79,9 +79,7 @@ constexpr int kOffRed = kOffCounts + kPosPerLane * 8 * 4;
 constexpr int kOffFlag = kOffRed + 2 * 2 * 32 * 4;
 constexpr int kLdsBytes = kOffFlag + 16;               // 157328
 static_assert(kOffPX + kPXB <= kStageBytes, "P overlaps the slot list");
-constexpr int kORow = kLatent + 4;                     // staged output row (floats; the pad spreads banks)
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
-static_assert(32 * kORow * 4 <= kOffX, "output staging overlaps the exchange");
 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -306,15 +304,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     // take consecutive 16-byte chunks of a head's row), the page-table entries
     // once the list is back, the queries staged in LDS (the K tiles are not in
     // use yet; rows padded so the fragment reads are conflict-free), the slots.
-    // All 64 head rows are staged at once (fp32 ones fill most of the LDS;
-    // nothing else lives in it yet but the slot list, which lies beyond).
+    // All 64 head rows are staged at once: bf16 ones in the third K tile and
+    // the exchange areas (free until the first tile's scores), so the first
+    // two tiles can be dequantized while the score wavefronts still read the
+    // queries; fp32 ones fill most of the LDS (the slot list lies beyond), and
+    // a barrier separates their last read from the first K-tile store.
     constexpr int kQE = QF32 ? 4 : 2;                      // bytes per query element
     constexpr int kQRow = kD * kQE + 16;                   // staged head row
     constexpr int kQH = 64;                                // heads staged
+    const uint32_t Lq = QF32 ? L : L + 2 * kKTileB;        // staging base
     constexpr int kQChunks = kD * kQE / 16;                // 16-byte chunks per head row
     constexpr int kQPer = kQH * kQChunks / kThreads;       // chunks per thread
     static_assert(kQH * kQChunks % kThreads == 0, "query chunks do not divide");
-    static_assert(kQH * kQRow <= kStageBytes, "staged queries overlap the slot list");
+    static_assert(kQH * kQRow <= (QF32 ? kStageBytes : kStageBytes - 2 * kKTileB), "staged queries overlap the slot list");
     // thread t loads head t / kTPH, 16-byte chunks t % kTPH +
     // kTPH i: one base address per thread, consecutive threads on consecutive
     // chunks of a head row
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         }
     };
     auto stage_q = [&](const u32x4_t (&qc)[kQPer]) {
-        const uint32_t dst = L + q_hh * kQRow + 16 * q_part;
+        const uint32_t dst = Lq + q_hh * kQRow + 16 * q_part;
 #pragma unroll
         for (int i = 0; i < kQPer; ++i) lds_st<u32x4_t>(dst + 16 * kTPH * i, qc[i]);
     };
@@ -367,33 +369,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
         __syncthreads();
     };
-    // one round of the output: 32 heads (staged in LDS) x 512 dims, every
-    // thread; one scalar base per round and 32-bit offsets per piece
-    auto store_round = [&](int hb) {
-        const int hb0 = h0 + 32 * hb;
-        const int n_live = min(32, p.n_heads - hb0);                  // heads of this round that exist
-        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)hb0 * kLatent;
-        if (p.out_h) {
-            _Float16 *ob = p.out_h + base;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {          // 32 heads x 128 pieces of 4 dims
-                const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
-                if (hh < n_live)
-                    *reinterpret_cast<half4_t *>(ob + (hh * kLatent + 4 * pc)) =
-                        __builtin_convertvector(lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc), half4_t);
-            }
-        } else {
-            float *ob = p.out + base;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int P = i * kThreads + tid, hh = P >> 7, pc = P & 127;
-                if (hh < n_live)
-                    *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pc)) =
-                        lds_ld<floatx4_t>(L + hh * (kORow * 4) + 16 * pc);
-            }
-        }
-    };
-
     if (w < 4) {
         // ================================================ score wavefronts
         const int hg = w & 1, half = w >> 1;
@@ -408,72 +383,71 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
 
         // queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head h0 +
         // 32hg + l32, dims kHd half + 16 ks + 8 g .. +7 for ks < kKs.  The
-        // power-of-two scale qs puts the head's largest |q| (over all dims: the
-        // two halves agree through LDS) in [2^13, 2^14): exact in fp16 for bf16
-        // queries; fp32 queries get a hi and a lo fp16 part.  The staged
-        // fragment is read twice, for the maximum and then for the conversion,
-        // so it never occupies registers beside its fp16 form.
+        // power-of-two scale qs puts the largest |q| of the head's half in
+        // [2^13, 2^14): exact in fp16 for bf16 queries; fp32 queries get a hi
+        // and a lo fp16 part.  Each half has its own scale: its partial scores
+        // are multiplied by score_mul = sm_scale log2(e) / qs before the two
+        // halves are added, so no exchange between them is needed here.
         half8_t qb[kKs];
         half8_t ql[QF32 ? kKs : 1];
         float score_mul = 0.0f;
         {
-            const uint32_t qf = L + (32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
-            auto frag_max = [&]() {
-                float qmax = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    if constexpr (QF32) {
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
-                            qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                                                                         __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
-                        }
-                    } else {
-                        const u32x4_t v = lds_ld<u32x4_t>(qf + 32 * ks);
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[c] << 16)),
-                                                                         __builtin_fabsf(__uint_as_float(v[c] & 0xFFFF0000u))));
-                    }
-                }
-                qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
-                if (g == 0) red[(hg * 2 + half) * 32 + l32] = qmax;
-            };
-            auto frag_convert = [&]() {
-                const float qmax = __builtin_fmaxf(red[(hg * 2) * 32 + l32], red[(hg * 2 + 1) * 32 + l32]);
+            const uint32_t qf = Lq + (32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
+            auto scale_of = [&](float qmax) {
+                qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));   // lanes l and l ^ 32: the same head
                 int ex = 0;
                 if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
                 const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
                 score_mul = p.score_mul / qs;
+                return qs;
+            };
+            if constexpr (QF32) {
+                // read twice, for the maximum and for the conversion, so the
+                // fp32 fragment never occupies registers beside its fp16 form
+                float qmax = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    if constexpr (QF32) {
+                for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+                    for (int j = 0; j < 2; ++j) {
+                        const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+                        qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                                     __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+                    }
+                const float qs = scale_of(qmax);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float x = v[e] * qs;
-                                const _Float16 hi = (_Float16)x;
-                                qb[ks][4 * j + e] = hi;
-                                ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
-                            }
-                        }
-                    } else {
-                        const u32x4_t v = lds_ld<u32x4_t>(qf + 32 * ks);
+                for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            qb[ks][2 * c] = (_Float16)(__uint_as_float(v[c] << 16) * qs);
-                            qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[c] & 0xFFFF0000u) * qs);
+                    for (int j = 0; j < 2; ++j) {
+                        const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = v[e] * qs;
+                            const _Float16 hi = (_Float16)x;
+                            qb[ks][4 * j + e] = hi;
+                            ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
                         }
                     }
+                __syncthreads();                   // the first K tiles overwrite the staged queries
+            } else {
+                u32x4_t v[kKs];
+                float qmax = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) {
+                    v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[ks][c] << 16)),
+                                                                     __builtin_fabsf(__uint_as_float(v[ks][c] & 0xFFFF0000u))));
                 }
-            };
-            frag_max();
-            __syncthreads();
-            frag_convert();
-            __syncthreads();                       // the staged queries may be overwritten
+                const float qs = scale_of(qmax);
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        qb[ks][2 * c] = (_Float16)(__uint_as_float(v[ks][c] << 16) * qs);
+                        qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[ks][c] & 0xFFFF0000u) * qs);
+                    }
+            }
         }
 
         // score operand (A of S^T = K Q^T): row l32, chunk kHc half + 2 ks + g;
@@ -520,18 +494,20 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             }
             sacc = acc;
         };
-        // the partner's 16 rows to it, ours kept (half is scalar: no lane mask)
+        // the partner's 16 rows to it, ours kept, both in log2 units (times
+        // this half's score_mul; half is scalar: no lane mask)
         auto exchange = [&]() {
+            const float sm = score_mul;
             if (half == 0) {
-                lds_st<floatx4_t>(x_w, floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]});
-                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]});
-                own0 = floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]};
-                own1 = floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]};
+                lds_st<floatx4_t>(x_w, floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]} * sm);
+                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]} * sm);
+                own0 = floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]} * sm;
+                own1 = floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]} * sm;
             } else {
-                lds_st<floatx4_t>(x_w, floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]});
-                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]});
-                own0 = floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]};
-                own1 = floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]};
+                lds_st<floatx4_t>(x_w, floatx4_t{sacc[0], sacc[1], sacc[2], sacc[3]} * sm);
+                lds_st<floatx4_t>(x_w + 16, floatx4_t{sacc[4], sacc[5], sacc[6], sacc[7]} * sm);
+                own0 = floatx4_t{sacc[8], sacc[9], sacc[10], sacc[11]} * sm;
+                own1 = floatx4_t{sacc[12], sacc[13], sacc[14], sacc[15]} * sm;
             }
         };
         // scores of this lane's rows 16 half + 8 (v / 4) + 4 g + v % 4: our
@@ -550,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             float raw[8], e[8];
             row_raw(x0, x1, raw);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+            for (int v = 0; v < 8; ++v) e[v] = raw[v] - m_ref;
             if (lim < kTile) {                     // scalar
 #pragma unroll
                 for (int v = 0; v < 8; ++v)
@@ -601,10 +577,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                     for (int j = 0; j < 4; ++j) raw[4 + j] = own1[j] + x1[j];
                 if constexpr (ks == 4)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+                    for (int v = 0; v < 4; ++v) e[v] = raw[v] - m_ref;
                 if constexpr (ks == 5)
 #pragma unroll
-                    for (int v = 4; v < 8; ++v) e[v] = __builtin_fmaf(raw[v], score_mul, -m_ref);
+                    for (int v = 4; v < 8; ++v) e[v] = raw[v] - m_ref;
                 if constexpr (ks == 6) {
                     if (lim < kTile) {             // scalar: the chunk's last two tiles only
 #pragma unroll
@@ -686,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                     const int lim = tile_lim(0);
 #pragma unroll
                     for (int v = 0; v < 8; ++v)
-                        if (row_of(v) < lim) tmax = __builtin_fmaxf(tmax, raw[v] * score_mul);
+                        if (row_of(v) < lim) tmax = __builtin_fmaxf(tmax, raw[v]);
                     tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
                     if (g == 0) red[(hg * 2 + half) * 32 + l32] = tmax;
                     __syncthreads();
@@ -714,8 +690,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         }
 
         if (err && p.err_word) atomicOr(p.err_word, err);
-        // row sums: the two lanes of a head, then the two halves
-        __syncthreads();
+        // row sums: the two lanes of a head, then (after the barrier the P.V
+        // wavefronts wait on too) the two halves.  red[] was last read before
+        // the passes' final barrier.
         {
             const float l2 = l_run + __shfl_xor(l_run, 32);
             if (g == 0) red[(hg * 2 + half) * 32 + l32] = l2;
@@ -728,17 +705,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
             p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
         }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {           // the same two barriers per round as the P.V wavefronts
-            __syncthreads();                       // the previous round's stores are done
-            __syncthreads();                       // the P.V wavefronts have staged 32 heads
-            store_round(hb);
-        }
     } else {
         // ================================================ P.V wavefronts
         const int dq = w - 4;
-        __syncthreads();                           // the score wavefronts convert the queries
-        __syncthreads();
+        if constexpr (QF32) __syncthreads();       // the score wavefronts have read the staged queries
         // parts 8..15 of a tile's rows, no rope; with fp32 queries also parts
         // 0..7 with the rope (unit 1)
         constexpr int kUnits = QF32 ? 2 : 1;
@@ -844,23 +814,37 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         }
 
         if (err && p.err_word) atomicOr(p.err_word, err);
-        __syncthreads();
         __syncthreads();                           // the row sums are in red[]
-        const uint32_t ow = L + l32 * (kORow * 4) + 4 * (128 * dq + 4 * g);
+        // O = O_acc / l straight from the accumulators: lane (l32, g) of
+        // o[md][hb] holds head 32 hb + l32, dims 128 dq + 32 md + 8 vq + 4 g
+        // .. +3 in registers 4 vq .. 4 vq + 3 (the lanes g = 0, 1 of a head
+        // fill 32 contiguous bytes, four vq a 128-byte line)
+        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride;
+        const int dim0 = 128 * dq + 4 * g;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
+            const int head = h0 + 32 * hb + l32;
             const float l_tot = red[(hb * 2) * 32 + l32] + red[(hb * 2 + 1) * 32 + l32];
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            __syncthreads();                       // the previous round's stores have read the staging area
+            if (head >= p.n_heads) continue;
+            const int64_t ho = base + (int64_t)head * kLatent + dim0;
+            if (p.out_h) {
 #pragma unroll
-            for (int md = 0; md < 4; ++md)
+                for (int md = 0; md < 4; ++md)
 #pragma unroll
-                for (int vq = 0; vq < 4; ++vq)
-                    lds_st<floatx4_t>(ow + 4 * (32 * md + 8 * vq),
-                                      floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
-                                                o[md][hb][4 * vq + 3]} * inv);
-            __syncthreads();
-            store_round(hb);
+                    for (int vq = 0; vq < 4; ++vq)
+                        *reinterpret_cast<half4_t *>(p.out_h + ho + 32 * md + 8 * vq) = __builtin_convertvector(
+                            floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
+                                      o[md][hb][4 * vq + 3]} * inv, half4_t);
+            } else {
+#pragma unroll
+                for (int md = 0; md < 4; ++md)
+#pragma unroll
+                    for (int vq = 0; vq < 4; ++vq)
+                        *reinterpret_cast<floatx4_t *>(p.out + ho + 32 * md + 8 * vq) =
+                            floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
+                                      o[md][hb][4 * vq + 3]} * inv;
+            }
         }
     }
 }
