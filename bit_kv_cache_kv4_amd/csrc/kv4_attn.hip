@@ -76,8 +76,15 @@ constexpr int kStageBytes = 64 * (kDim * 4 + 16);      // 148480: all 64 fp32 qu
 constexpr int kOffSlots = kStageBytes;                 // 148480
 constexpr int kOffCounts = kOffSlots + kSlotCap * 4;   // 156672
 constexpr int kOffRed = kOffCounts + kPosPerLane * 8 * 4;
-constexpr int kOffFlag = kOffRed + 2 * 2 * 32 * 4;
-constexpr int kLdsBytes = kOffFlag + 16;               // 157328
+constexpr int kOffRowSum = kOffRed + 2 * 2 * 32 * 4;
+constexpr int kOffRowRef = kOffRowSum + 2 * 2 * 32 * 4;
+constexpr int kOffFlag = kOffRowRef + 2 * 32 * 4;
+constexpr int kLdsBytes = kOffFlag + 16;               // 158096
+// the output staged for its coalesced store: 64 head rows of 512 fp32 (row
+// stride 2064 bytes) or fp16 (1032 bytes) values; the strides put the 16- or
+// 8-byte stores of 32 consecutive heads on distinct banks
+constexpr int kORowF = kLatent * 4 + 16, kORowH = kLatent * 2 + 8;
+static_assert(64 * kORowF <= kStageBytes, "output staging overlaps the slot list");
 static_assert(kOffPX + kPXB <= kStageBytes, "P overlaps the slot list");
 constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 P above its reference
 
@@ -278,6 +285,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     int32_t *slots = reinterpret_cast<int32_t *>(lds + kOffSlots);
     int32_t *counts = reinterpret_cast<int32_t *>(lds + kOffCounts);
     float *red = reinterpret_cast<float *>(lds + kOffRed);
+    float *row_sum = reinterpret_cast<float *>(lds + kOffRowSum);   // [head group][half][head]: the halves' l
+    float *row_ref = reinterpret_cast<float *>(lds + kOffRowRef);   // [head group][head]: the reference m_ref
     int32_t *flag = reinterpret_cast<int32_t *>(lds + kOffFlag);
     const uint32_t L = lds_addr(lds);
 
@@ -369,6 +378,36 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
         __syncthreads();
     };
+    // the output of this task's live heads from its staging rows: 16-byte
+    // (fp32) or 8-byte (fp16) pieces, consecutive threads on consecutive
+    // pieces of a head row; the head of piece i is the same in a wavefront
+    auto store_out = [&]() {
+        const int n_live = min(64, p.n_heads - h0);
+        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)h0 * kLatent;
+        const int pc = tid & 127;
+        if (p.out_h) {
+            _Float16 *ob = p.out_h + base;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int hh = 4 * i + (tid >> 7);
+                if (hh < n_live)
+                    *reinterpret_cast<half4_t *>(ob + (hh * kLatent + 4 * pc)) = lds_ld<half4_t>(L + hh * kORowH + 8 * pc);
+            }
+        } else {
+            float *ob = p.out + base;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int hh = 8 * i + (tid >> 6);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int pj = 64 * j + (tid & 63);
+                    if (hh < n_live)
+                        *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)) = lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj);
+                }
+            }
+        }
+    };
+
     if (w < 4) {
         // ================================================ score wavefronts
         const int hg = w & 1, half = w >> 1;
@@ -680,6 +719,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                 }
             }
             if (need_redo) *flag = 1;
+            {   // this pass's row sums and reference (the final ones unless a second pass follows)
+                const float l2 = l_run + __shfl_xor(l_run, 32);
+                if (g == 0) row_sum[(hg * 2 + half) * 32 + l32] = l2;
+                if (g == 0 && half == 0) row_ref[hg * 32 + l32] = have_ref ? m_ref : 0.0f;
+            }
             __syncthreads();
             if (pass == 1 || *flag == 0) break;    // uniform: read after the barrier
             // second pass: the exact maximum of every head as its reference
@@ -690,21 +734,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         }
 
         if (err && p.err_word) atomicOr(p.err_word, err);
-        // row sums: the two lanes of a head, then (after the barrier the P.V
-        // wavefronts wait on too) the two halves.  red[] was last read before
-        // the passes' final barrier.
-        {
-            const float l2 = l_run + __shfl_xor(l_run, 32);
-            if (g == 0) red[(hg * 2 + half) * 32 + l32] = l2;
-        }
-        __syncthreads();
-        const float l_tot = red[(hg * 2) * 32 + l32] + red[(hg * 2 + 1) * 32 + l32];
-        const int head = h0 + 32 * hg + l32;
-        if (half == 0 && g == 0 && head < p.n_heads && p.lse) {
-            const float m_fin = have_ref ? m_ref : 0.0f;
-            const float lse = l_tot > 0.0f ? (m_fin + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -__builtin_inff();
-            p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
-        }
+        __syncthreads();                           // the P.V wavefronts have staged the output
+        store_out();
     } else {
         // ================================================ P.V wavefronts
         const int dq = w - 4;
@@ -814,38 +845,43 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         }
 
         if (err && p.err_word) atomicOr(p.err_word, err);
-        __syncthreads();                           // the row sums are in red[]
-        // O = O_acc / l straight from the accumulators: lane (l32, g) of
-        // o[md][hb] holds head 32 hb + l32, dims 128 dq + 32 md + 8 vq + 4 g
-        // .. +3 in registers 4 vq .. 4 vq + 3 (the lanes g = 0, 1 of a head
-        // fill 32 contiguous bytes, four vq a 128-byte line)
-        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride;
-        const int dim0 = 128 * dq + 4 * g;
+        // O = O_acc / l (the row sums were written before the passes' last
+        // barrier) staged for the coalesced store: lane (l32, g) of o[md][hb]
+        // holds head 32 hb + l32, dims 128 dq + 32 md + 8 vq + 4 g .. +3 in
+        // registers 4 vq .. 4 vq + 3
+        auto stage = [&](auto half_out) {
+            constexpr bool kH = decltype(half_out)::value;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const int head = h0 + 32 * hb + l32;
-            const float l_tot = red[(hb * 2) * 32 + l32] + red[(hb * 2 + 1) * 32 + l32];
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            if (head >= p.n_heads) continue;
-            const int64_t ho = base + (int64_t)head * kLatent + dim0;
-            if (p.out_h) {
+            for (int hb = 0; hb < 2; ++hb) {
+                const float l_tot = row_sum[(hb * 2) * 32 + l32] + row_sum[(hb * 2 + 1) * 32 + l32];
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const uint32_t row = L + (32 * hb + l32) * (kH ? kORowH : kORowF);
 #pragma unroll
                 for (int md = 0; md < 4; ++md)
 #pragma unroll
-                    for (int vq = 0; vq < 4; ++vq)
-                        *reinterpret_cast<half4_t *>(p.out_h + ho + 32 * md + 8 * vq) = __builtin_convertvector(
-                            floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
-                                      o[md][hb][4 * vq + 3]} * inv, half4_t);
-            } else {
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int dim = 128 * dq + 32 * md + 8 * vq + 4 * g;
+                        const floatx4_t v = floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
+                                                      o[md][hb][4 * vq + 3]} * inv;
+                        if constexpr (kH) lds_st<half4_t>(row + 2 * dim, __builtin_convertvector(v, half4_t));
+                        else lds_st<floatx4_t>(row + 4 * dim, v);
+                    }
+            }
+        };
+        if (p.out_h) stage(std::true_type{});
+        else stage(std::false_type{});
+        if (dq == 0 && g == 0 && p.lse) {          // lse = ln(l) + m_ref ln 2 of heads 32 hb + l32
 #pragma unroll
-                for (int md = 0; md < 4; ++md)
-#pragma unroll
-                    for (int vq = 0; vq < 4; ++vq)
-                        *reinterpret_cast<floatx4_t *>(p.out + ho + 32 * md + 8 * vq) =
-                            floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
-                                      o[md][hb][4 * vq + 3]} * inv;
+            for (int hb = 0; hb < 2; ++hb) {
+                const int head = h0 + 32 * hb + l32;
+                const float l_tot = row_sum[(hb * 2) * 32 + l32] + row_sum[(hb * 2 + 1) * 32 + l32];
+                const float lse = l_tot > 0.0f ? (row_ref[hb * 32 + l32] + __builtin_log2f(l_tot)) * 0.69314718055994530942f
+                                               : -__builtin_inff();
+                if (head < p.n_heads) p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
             }
         }
+        __syncthreads();
+        store_out();
     }
 }
 
