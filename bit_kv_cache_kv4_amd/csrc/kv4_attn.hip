@@ -308,11 +308,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
     uint32_t err = 0;
 
-    // ---- Prologue, arranged so its memory round trips overlap: the first
-    // chunk's list entries, this row's queries (coalesced: consecutive threads
-    // take consecutive 16-byte chunks of a head's row), the page-table entries
-    // once the list is back, the queries staged in LDS (the K tiles are not in
-    // use yet; rows padded so the fragment reads are conflict-free), the slots.
+    // ---- Prologue.  Three dependent round trips (list entries, page-table
+    // entries, the first rows) come before the first tile, so nothing may queue
+    // ahead of them: the list, then the page-table entries once it is back,
+    // then this row's queries (coalesced: consecutive threads take consecutive
+    // 16-byte chunks of a head's row; 74 KB, whose loads would otherwise hold
+    // up the page-table loads), the slots packed, the first gathers issued,
+    // and only then the queries staged in LDS (rows padded so the fragment
+    // reads are conflict-free).
     // All 64 head rows are staged at once: bf16 ones in the third K tile and
     // the exchange areas (free until the first tile's scores), so the first
     // two tiles can be dequantized while the score wavefronts still read the
@@ -350,14 +353,22 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
 
     int32_t pos[kPosPerLane], phys[kPosPerLane];
     const int first_hi = min(e_hi, e_lo + kSlotCap);
-    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);   // issued first: loads complete in order
+    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
     u32x4_t qc[kQPer];
-    load_q(qc);
-    load_pages(p, lc, pos, phys);
-    stage_q(qc);
+    if constexpr (QF32) {
+        // fp32 rows (147 KB) are staged before the roles split: their 72
+        // registers per thread must not stay live into the roles
+        load_q(qc);
+        load_pages(p, lc, pos, phys);
+        stage_q(qc);
+    } else {
+        load_pages(p, lc, pos, phys);
+        load_q(qc);                                // after the page-table loads: it must not delay them
+    }
     int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
     if (tid == 0) *flag = 0;
-    __syncthreads();
+    __syncthreads();                               // slots[] complete; with bf16 queries each role issues
+                                                   // its first gathers, then stages its queries
 
     const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
     int n_t = 0, n_real = 0, last_rows = kTile;   // tiles (even), tiles holding entries, rows of the last
@@ -418,6 +429,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         if (kDq && nv > 0) {                       // tile 1 exists: chunks have an even number of tiles
             gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
             gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+        }
+        if constexpr (!QF32) {
+            stage_q(qc);
+            __syncthreads();                       // every head row staged
         }
 
         // queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head h0 +
@@ -739,7 +754,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     } else {
         // ================================================ P.V wavefronts
         const int dq = w - 4;
-        if constexpr (QF32) __syncthreads();       // the score wavefronts have read the staged queries
         // parts 8..15 of a tile's rows, no rope; with fp32 queries also parts
         // 0..7 with the rope (unit 1)
         constexpr int kUnits = QF32 ? 2 : 1;
@@ -756,6 +770,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
         if (nv > 0) {
             gather_units(0, G0);
             gather_units(1, G1);
+        }
+        if constexpr (!QF32) {
+            stage_q(qc);
+            __syncthreads();                       // every head row staged
+        } else {
+            __syncthreads();                       // the score wavefronts have read the staged queries
         }
         // transposing reads (A of O^T = V^T P^T): this lane names row j4 + 4g
         // (+8 for the second read of a k-step, +16 for the second k-step), 8
@@ -885,15 +905,485 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     }
 }
 
+// ------------------------------------------------ bf16 queries
+// Same workgroup, task, front end, gathers and K-tile layout as above, with the
+// score wavefronts arranged so that each owns whole scores: wavefront w < 4 =
+// (head group hg = w % 2 of 32 heads, row half rh = w / 2 of each tile) holds
+// the queries of its 32 heads over all kD dims (144 registers) and computes
+// S^T[16 rows x 32 heads] with v_mfma_f32_16x16x32_f16, two head blocks of 16
+// sharing each K operand read.  With no partial scores to swap, the softmax of
+// a tile follows its scores in the same phase, and every tile takes one
+// barrier:
+//   iteration t: scores and softmax of t + 1 (P into P buffer (t + 1) % 2),
+//                P.V of t (from P buffer t % 2), dequantization of t + 2 by
+//                both roles, gathers of t + 4; barrier.
+// Three K tiles are in use in an iteration (t, t + 1, t + 2), so the three
+// buffers rotate as before.  K reads for the scores stay at two per element
+// (one per head group) and the swap's 16 KB of LDS traffic per tile is gone.
+constexpr int kOffP2 = kNBuf * kKTileB;                // two P buffers
+static_assert(kOffP2 + 2 * kPXB <= kStageBytes, "P buffers overlap the slot list");
+
+__device__ __forceinline__ floatx4_t mfma16(half8_t a, half8_t b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p) {
+    constexpr int kD = ROPE ? kDim : kLatent;
+    constexpr int kKs = kD / 32;               // MFMA k-steps of 32 dims over the whole row
+    constexpr int kAhead = 4;                  // score operands read ahead of their MFMAs
+    constexpr int kTrAhead = 4;                // P.V operand pairs read ahead
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + kOffSlots);
+    int32_t *counts = reinterpret_cast<int32_t *>(lds + kOffCounts);
+    float *red = reinterpret_cast<float *>(lds + kOffRed);          // [hg][rh][head]: reference agreement
+    float *row_sum = reinterpret_cast<float *>(lds + kOffRowSum);   // [hg][rh][head]: the row halves' l
+    float *row_ref = reinterpret_cast<float *>(lds + kOffRowRef);   // [hg][head]: the reference m_ref
+    int32_t *flag = reinterpret_cast<int32_t *>(lds + kOffFlag);
+    const uint32_t L = lds_addr(lds);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int gr = tid & 31, gp = tid >> 5;
+    const int r = blockIdx.x, split = blockIdx.y, h0 = blockIdx.z * 64;
+
+    const int n_tiles = (p.k + kTile - 1) / kTile;
+    const int t_lo = split * p.tiles_per_split;
+    const int t_hi = min(n_tiles, t_lo + p.tiles_per_split);
+    const int e_lo = t_lo * kTile;
+    const int e_hi = min(p.k, t_hi * kTile);
+
+    const ListCtx lc = list_ctx(p, r);
+    const uint8_t *stand_in = reinterpret_cast<const uint8_t *>(p.q);
+    uint32_t err = 0;
+
+    // ---- Prologue.  Three dependent round trips (list entries, page-table
+    // entries, the first rows) come before the first tile, so nothing queues
+    // ahead of them: the list, the page-table entries once it is back, then
+    // this row's queries (74 KB: consecutive threads take consecutive 16-byte
+    // chunks of a head's row), the slots packed, each role's first gathers,
+    // and only then the queries staged in LDS, in the third K tile and the P
+    // buffers (untouched until the first tile's softmax; rows padded by 16
+    // bytes).
+    constexpr int kQRow = kD * 2 + 16;
+    constexpr int kQChunks = kD * 2 / 16;
+    constexpr int kTPH = kThreads / 64;                    // threads per head row
+    constexpr int kQPer = kQChunks / kTPH;                 // chunks per thread
+    static_assert(kQChunks == kTPH * kQPer, "query chunks do not divide");
+    static_assert(2 * kKTileB + 64 * kQRow <= kStageBytes, "staged queries overlap the slot list");
+    const uint32_t Lq = L + 2 * kKTileB;
+    const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * 2;
+    const int q_hh = tid / kTPH, q_part = tid % kTPH;
+    u32x4_t qc[kQPer];
+
+    int32_t pos[kPosPerLane], phys[kPosPerLane];
+    const int first_hi = min(e_hi, e_lo + kSlotCap);
+    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
+    load_pages(p, lc, pos, phys);
+    {
+        const int head = h0 + q_hh;
+        const uint8_t *src = qr + (int64_t)min(head, p.n_heads - 1) * p.q_head_stride * 2 + 16 * q_part;
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) {
+            qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
+            if (head >= p.n_heads) qc[i] = u32x4_t{0, 0, 0, 0};
+        }
+    }
+    int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    auto stage_q = [&]() {
+        const uint32_t dst = Lq + q_hh * kQRow + 16 * q_part;
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) lds_st<u32x4_t>(dst + 16 * kTPH * i, qc[i]);
+    };
+
+    const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
+    int n_t = 0, n_real = 0, last_rows = kTile;
+    bool have_ref = false;
+    auto chunk_tiles = [&]() {
+        n_real = (nv + kTile - 1) / kTile;
+        n_t = (n_real + 1) & ~1;
+        last_rows = nv - kTile * (n_real - 1);
+    };
+    auto tile_lim = [&](int t) { return t < n_real - 1 ? kTile : t == n_real - 1 ? last_rows : 0; };
+    auto fresh_chunk = [&](int c_lo, int c_hi) {
+        __syncthreads();
+        load_positions(lc, c_lo, c_hi, tid, pos);
+        load_pages(p, lc, pos, phys);
+        nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
+        __syncthreads();
+    };
+    auto store_out = [&]() {
+        const int n_live = min(64, p.n_heads - h0);
+        const int64_t base = (int64_t)split * p.out_split_stride + (int64_t)r * p.out_row_stride + (int64_t)h0 * kLatent;
+        const int pc = tid & 127;
+        if (p.out_h) {
+            _Float16 *ob = p.out_h + base;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int hh = 4 * i + (tid >> 7);
+                if (hh < n_live)
+                    *reinterpret_cast<half4_t *>(ob + (hh * kLatent + 4 * pc)) = lds_ld<half4_t>(L + hh * kORowH + 8 * pc);
+            }
+        } else {
+            float *ob = p.out + base;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int hh = 8 * i + (tid >> 6);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int pj = 64 * j + (tid & 63);
+                    if (hh < n_live)
+                        *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)) = lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj);
+                }
+            }
+        }
+    };
+
+    if (w < 4) {
+        // ================================================ score wavefronts
+        const int hg = w & 1, rh = w >> 1;
+        const int l16 = lane & 15, q4 = lane >> 4;
+        // parts 0..7 of a tile's rows, with the rope
+        GSet<ROPE> G0, G1;
+        if (nv > 0) {
+            gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+            gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+        }
+        stage_q();
+        __syncthreads();                           // every head row staged
+
+        // queries: B operand of S^T = K Q^T.  Lane (l16, q4) holds head h0 +
+        // 32 hg + 16 hb + l16, dims 32 ks + 8 q4 .. +7.  The power-of-two scale
+        // qs puts the head's largest |q| in [2^13, 2^14), exact in fp16;
+        // score_mul = sm_scale log2(e) / qs turns scores into log2 units.
+        half8_t qb[2][kKs];
+        float score_mul[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const uint32_t qf = Lq + (32 * hg + 16 * hb + l16) * kQRow + 16 * q4;
+            float qmax = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {     // read twice (maximum, conversion): fewer live registers
+                const u32x4_t v = lds_ld<u32x4_t>(qf + 64 * ks);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[c] << 16)),
+                                                                 __builtin_fabsf(__uint_as_float(v[c] & 0xFFFF0000u))));
+            }
+            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 16));
+            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
+            int ex = 0;
+            if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
+            const float qs = __builtin_ldexpf(1.0f, 14 - ex);
+            score_mul[hb] = p.score_mul / qs;
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+                const u32x4_t v = lds_ld<u32x4_t>(qf + 64 * ks);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    qb[hb][ks][2 * c] = (_Float16)(__uint_as_float(v[c] << 16) * qs);
+                    qb[hb][ks][2 * c + 1] = (_Float16)(__uint_as_float(v[c] & 0xFFFF0000u) * qs);
+                }
+            }
+        }
+
+        // score operand (A of 16x16x32): row 16 rh + l16, chunk 4 ks + q4
+        const uint32_t a_off = q4 * kChunkB + 16 * ((16 * rh + l16) ^ (4 * q4));
+        // P of head 32 hg + 16 hb + l16, rows 16 rh + 4 q4 + 0..3: 8 contiguous
+        // bytes in the P.V operand order (row bits 2 and 3 swapped)
+        const uint32_t px_w = L + kOffP2 + (32 * hg + l16) * kPXHead + 2 * (16 * rh + 8 * (q4 & 1) + 4 * (q4 >> 1));
+        const int row0 = 16 * rh + 4 * q4;         // this lane's first row
+
+        float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
+        float m_max[2] = {-__builtin_inff(), -__builtin_inff()};
+        float l_run[2] = {0.0f, 0.0f};
+        bool need_redo = false;
+
+        auto scores = [&](uint32_t kb, floatx4_t (&acc)[2]) {
+            const uint32_t a0 = kb + a_off;
+            half8_t a[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>(a0 + 4 * kChunkB * i);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] = floatx4_t{0, 0, 0, 0};
+            acc[1] = floatx4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+                const half8_t cur = a[ks % kAhead];
+                acc[0] = mfma16(cur, qb[0][ks], acc[0]);
+                acc[1] = mfma16(cur, qb[1][ks], acc[1]);
+                if (ks + kAhead < kKs) a[ks % kAhead] = lds_ld<half8_t>(a0 + 4 * kChunkB * (ks + kAhead));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // P = 2^(s - m_ref) of this lane's 4 rows x 2 heads into P buffer pb;
+        // rows >= lim are padding
+        auto softmax = [&](const floatx4_t (&acc)[2], int lim, int pb) {
+            float e[2][4];
+            float emax = -__builtin_inff();
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float hm = -__builtin_inff();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e[hb][i] = __builtin_fmaf(acc[hb][i], score_mul[hb], -m_ref[hb]);
+                    if (lim < kTile && row0 + i >= lim) e[hb][i] = -__builtin_inff();
+                    hm = __builtin_fmaxf(hm, e[hb][i]);
+                }
+                m_max[hb] = __builtin_fmaxf(m_max[hb], hm + m_ref[hb]);
+                emax = __builtin_fmaxf(emax, hm);
+            }
+            need_redo |= emax > kRefSlack;         // P could overflow fp16
+            const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                half4_t ph;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ph[i] = (_Float16)__builtin_amdgcn_exp2f(e[hb][i]);   // exp2(-inf) = 0
+                float ls = __builtin_amdgcn_fdot2(half2_t{ph[0], ph[1]}, one2, 0.0f, false);
+                ls = __builtin_amdgcn_fdot2(half2_t{ph[2], ph[3]}, one2, ls, false);
+                l_run[hb] += ls;
+                lds_st<half4_t>(px_w + pb * kPXB + hb * (16 * kPXHead), ph);
+            }
+        };
+        // phase: scores and softmax of t + 1, dequantization of t + 2 (latent
+        // dims 0..255 and the rope), gather of t + 4 (clamped to the chunk's
+        // last tile: a harmless repeat that keeps the loads unconditional)
+        auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bB, uint32_t bC) {
+            const int32_t next = slots[min(t + 4, n_t - 1) * kTile + gr];
+            if (t + 1 < n_t) {
+                floatx4_t acc[2];
+                scores(bB, acc);
+                softmax(acc, tile_lim(t + 1), (t + 1) & 1);
+            }
+            if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, true, G);
+            gather_set<ROPE>(p.pool, stand_in, next, gp, G);
+            __syncthreads();
+        };
+
+        for (int pass = 0; pass < 2; ++pass) {
+            l_run[0] = l_run[1] = 0.0f;
+            for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
+                const int c_hi = min(e_hi, c_lo + kSlotCap);
+                if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) fresh_chunk(c_lo, c_hi);
+                chunk_tiles();
+                if (n_real == 0) continue;         // nothing valid in this chunk (uniform)
+                if (pass == 1 || c_lo != e_lo) {   // the first chunk's were gathered before the passes
+                    gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+                    gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+                }
+                dequant_set<ROPE>(K0, gr, gp, true, G0);
+                gather_set<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, G0);
+                dequant_set<ROPE>(K1, gr, gp, true, G1);
+                gather_set<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, G1);
+                __syncthreads();                   // tiles 0 and 1 in LDS
+                {
+                    floatx4_t acc[2];
+                    scores(K0, acc);
+                    if (!have_ref) {               // first tile with entries: each head's reference
+                        const int lim = tile_lim(0);
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb) {
+                            float tmax = -__builtin_inff();
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (row0 + i < lim) tmax = __builtin_fmaxf(tmax, acc[hb][i] * score_mul[hb]);
+                            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
+                            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+                            if (q4 == 0) red[(hg * 2 + rh) * 32 + 16 * hb + l16] = tmax;
+                        }
+                        __syncthreads();
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb)
+                            m_ref[hb] = __builtin_fmaxf(red[(hg * 2) * 32 + 16 * hb + l16], red[(hg * 2 + 1) * 32 + 16 * hb + l16]);
+                        have_ref = true;
+                    }
+                    softmax(acc, tile_lim(0), 0);
+                }
+                __syncthreads();                   // P of tile 0 in P buffer 0
+                uint32_t bA = K0, bB = K1, bC = K2;
+                for (int t = 0; t < n_t; t += 2) {
+                    iteration(t, G0, bB, bC);      // G0: tile t + 2 -> bC, then t + 4
+                    iteration(t + 1, G1, bC, bA);  // G1: tile t + 3 -> bA, then t + 5
+                    const uint32_t a0 = bA;        // tiles t + 2, t + 3, t + 4 go to bC, bA, bB
+                    bA = bC;
+                    bC = bB;
+                    bB = a0;
+                }
+            }
+            if (need_redo) *flag = 1;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {       // this pass's row sums and reference
+                float l2 = l_run[hb] + __shfl_xor(l_run[hb], 16);
+                l2 += __shfl_xor(l2, 32);
+                if (q4 == 0) row_sum[(hg * 2 + rh) * 32 + 16 * hb + l16] = l2;
+                if (q4 == 0 && rh == 0) row_ref[hg * 32 + 16 * hb + l16] = have_ref ? m_ref[hb] : 0.0f;
+            }
+            __syncthreads();
+            if (pass == 1 || *flag == 0) break;    // uniform: read after the barrier
+            // second pass: the exact maximum of every head as its reference
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                float mm = __builtin_fmaxf(m_max[hb], __shfl_xor(m_max[hb], 16));
+                mm = __builtin_fmaxf(mm, __shfl_xor(mm, 32));
+                if (q4 == 0) red[(hg * 2 + rh) * 32 + 16 * hb + l16] = mm;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+                m_ref[hb] = __builtin_fmaxf(red[(hg * 2) * 32 + 16 * hb + l16], red[(hg * 2 + 1) * 32 + 16 * hb + l16]);
+        }
+
+        if (err && p.err_word) atomicOr(p.err_word, err);
+        __syncthreads();                           // the P.V wavefronts have staged the output
+        store_out();
+    } else {
+        // ================================================ P.V wavefronts
+        const int dq = w - 4;
+        // parts 8..15 of a tile's rows, no rope
+        GSet<ROPE> G0, G1;
+        auto gather_units = [&](int tile, GSet<ROPE> &G) {
+            gather_set<ROPE, false>(p.pool, stand_in, slots[tile * kTile + gr], gp, G);
+        };
+        if (nv > 0) {
+            gather_units(0, G0);
+            gather_units(1, G1);
+        }
+        stage_q();
+        __syncthreads();                           // every head row staged
+
+        // transposing reads (A of O^T = V^T P^T), as in the fp32-query kernel
+        const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), j4 = (lane >> 2) & 3;
+        const uint32_t tr_off0 = (16 * dq + cc) * kChunkB + 16 * (j4 + 4 * (g ^ (cc & 1)) + 8 * (cc >> 1)) + 8 * (lane & 1);
+        const uint32_t tr_off1 = (16 * dq + cc) * kChunkB + 16 * (j4 + 4 * (g ^ (cc & 1)) + 8 * (1 ^ (cc >> 1))) + 8 * (lane & 1);
+        const uint32_t px_r = L + kOffP2 + l32 * kPXHead + 2 * (8 * g);
+        floatx16_t o[4][2];
+
+        auto pv = [&](uint32_t kb, int pb) {
+            const uint32_t t0 = kb + tr_off0, t1 = kb + tr_off1;
+            half8_t pbv[2][2];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    pbv[hb][kk] = lds_ld<half8_t>(px_r + pb * kPXB + hb * (32 * kPXHead) + 32 * kk);
+            short4_t lo[kTrAhead], hi[kTrAhead];
+            auto issue = [&](int j) {
+                const int md = j & 3, kk = j >> 2;
+                lo[j % kTrAhead] = lds_read_tr16(t0 + 4 * kChunkB * md + 256 * kk);
+                hi[j % kTrAhead] = lds_read_tr16(t1 + 4 * kChunkB * md + 256 * kk);
+            };
+#pragma unroll
+            for (int j = 0; j < kTrAhead; ++j) issue(j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int md = j & 3, kk = j >> 2;
+                const half8_t a = __builtin_bit_cast(
+                    half8_t, __builtin_shufflevector(lo[j % kTrAhead], hi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
+                o[md][0] = mfma32(a, pbv[0][kk], o[md][0]);
+                o[md][1] = mfma32(a, pbv[1][kk], o[md][1]);
+                if (j + kTrAhead < 8) issue(j + kTrAhead);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // phase: P.V of t, dequantization of t + 2 (latent dims 256..511),
+        // gather of t + 4
+        auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bA, uint32_t bC) {
+            pv(bA, t & 1);
+            if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, false, G);
+            gather_units(min(t + 4, n_t - 1), G);
+            __syncthreads();
+        };
+
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int md = 0; md < 4; ++md) o[md][0] = o[md][1] = floatx16_t{};
+            for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
+                const int c_hi = min(e_hi, c_lo + kSlotCap);
+                if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) fresh_chunk(c_lo, c_hi);
+                chunk_tiles();
+                if (n_real == 0) continue;
+                if (pass == 1 || c_lo != e_lo) {
+                    gather_units(0, G0);
+                    gather_units(1, G1);
+                }
+                dequant_set<ROPE>(K0, gr, gp, false, G0);
+                gather_units(min(2, n_t - 1), G0);
+                dequant_set<ROPE>(K1, gr, gp, false, G1);
+                gather_units(min(3, n_t - 1), G1);
+                __syncthreads();                   // tiles 0 and 1 in LDS
+                if (!have_ref) {
+                    __syncthreads();               // the reference is agreed
+                    have_ref = true;
+                }
+                __syncthreads();                   // P of tile 0 in P buffer 0
+                uint32_t bA = K0, bB = K1, bC = K2;
+                for (int t = 0; t < n_t; t += 2) {
+                    iteration(t, G0, bA, bC);
+                    iteration(t + 1, G1, bB, bA);
+                    const uint32_t a0 = bA;
+                    bA = bC;
+                    bC = bB;
+                    bB = a0;
+                }
+            }
+            __syncthreads();
+            if (pass == 1 || *flag == 0) break;
+            __syncthreads();                       // the second pass's reference is agreed
+        }
+
+        if (err && p.err_word) atomicOr(p.err_word, err);
+        // O = O_acc / l staged for the coalesced store (row sums and the
+        // reference were written before the passes' last barrier)
+        auto stage = [&](auto half_out) {
+            constexpr bool kH = decltype(half_out)::value;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const float l_tot = row_sum[(hb * 2) * 32 + l32] + row_sum[(hb * 2 + 1) * 32 + l32];
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const uint32_t row = L + (32 * hb + l32) * (kH ? kORowH : kORowF);
+#pragma unroll
+                for (int md = 0; md < 4; ++md)
+#pragma unroll
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int dim = 128 * dq + 32 * md + 8 * vq + 4 * g;
+                        const floatx4_t v = floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
+                                                      o[md][hb][4 * vq + 3]} * inv;
+                        if constexpr (kH) lds_st<half4_t>(row + 2 * dim, __builtin_convertvector(v, half4_t));
+                        else lds_st<floatx4_t>(row + 4 * dim, v);
+                    }
+            }
+        };
+        if (p.out_h) stage(std::true_type{});
+        else stage(std::false_type{});
+        if (dq == 0 && g == 0 && p.lse) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int head = h0 + 32 * hb + l32;
+                const float l_tot = row_sum[(hb * 2) * 32 + l32] + row_sum[(hb * 2 + 1) * 32 + l32];
+                const float lse = l_tot > 0.0f ? (row_ref[hb * 32 + l32] + __builtin_log2f(l_tot)) * 0.69314718055994530942f
+                                               : -__builtin_inff();
+                if (head < p.n_heads) p.lse[(int64_t)split * p.lse_split_stride + (int64_t)r * p.lse_row_stride + head] = lse;
+            }
+        }
+        __syncthreads();
+        store_out();
+    }
+}
+
 hipError_t launch_sparse_mla(const AttnParams &p, bool q_f32, int32_t n_splits, hipStream_t stream) {
     if (p.n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)p.n_rows, (unsigned)n_splits, (unsigned)((p.n_heads + 63) / 64));
     if (p.rope_dims == kRope) {
         if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
-        else hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, dim3(kThreads), 0, stream, p);
     } else {
         if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
-        else hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
