@@ -70,16 +70,21 @@ constexpr int kPXHead = 80;                            // P of one head: 32 rows
 constexpr int kPXB = 64 * kPXHead;
 constexpr int kSlotCap = 2048;                         // entries translated per chunk
 constexpr int kPosPerLane = kSlotCap / kThreads;
-constexpr int kOffX = kNBuf * kKTileB;                 // 110592
-constexpr int kOffPX = kOffX + kXB;                    // 118784
-constexpr int kStageBytes = 64 * (kDim * 4 + 16);      // 148480: all 64 fp32 query rows (K tiles, X, P and spare)
-constexpr int kOffSlots = kStageBytes;                 // 148480
-constexpr int kOffCounts = kOffSlots + kSlotCap * 4;   // 156672
+// LDS: the small fixed areas first, at addresses below 64 KB that every LDS
+// instruction reaches through its immediate offset (no address register held
+// for them); then the K tiles and what shares their space; the slot list last.
+constexpr int kOffCounts = 0;                          // per-wavefront counts of valid entries
 constexpr int kOffRed = kOffCounts + kPosPerLane * 8 * 4;
 constexpr int kOffRowSum = kOffRed + 2 * 2 * 32 * 4;
 constexpr int kOffRowRef = kOffRowSum + 2 * 2 * 32 * 4;
 constexpr int kOffFlag = kOffRowRef + 2 * 32 * 4;
-constexpr int kLdsBytes = kOffFlag + 16;               // 158096
+constexpr int kOffK = 1536;                            // K tiles; offsets below are relative to it
+static_assert(kOffFlag + 16 <= kOffK, "small areas overlap the K tiles");
+constexpr int kOffX = kNBuf * kKTileB;                 // 110592
+constexpr int kOffPX = kOffX + kXB;                    // 118784
+constexpr int kStageBytes = 64 * (kDim * 4 + 16);      // 148480: all 64 fp32 query rows (K tiles, X, P and spare)
+constexpr int kOffSlots = kOffK + kStageBytes;         // 150016 (absolute)
+constexpr int kLdsBytes = kOffSlots + kSlotCap * 4;    // 158208
 // the output staged for its coalesced store: 64 head rows of 512 fp32 (row
 // stride 2064 bytes) or fp16 (1032 bytes) values; the strides put the 16- or
 // 8-byte stores of 32 consecutive heads on distinct banks
@@ -239,33 +244,46 @@ __device__ __forceinline__ void gather_set(const uint8_t *__restrict__ pool, con
     else G.rp = u32x2_t{0, 0};
 }
 
+// The dequantization in pieces, so a caller can spread them between its
+// MFMAs: the part's two block scales (E4M3 -> fp16, exact; 0 for a skipped
+// entry), one 8-dim chunk (the conversion at scale 1 is exact, and so is the
+// product with the block scale), and the rope chunk.
+template <bool ROPE>
+__device__ __forceinline__ half2_t dq_scales(const GSet<ROPE> &G, int gp) {
+    const uint32_t sc = G.valid ? G.sc >> (16 * (gp & 1)) : 0u;                     // this part's two scales
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+}
+// chunk 4gp + i: dims 32gp + 8i .. +7, block 2gp + i / 2
+template <bool ROPE>
+__device__ __forceinline__ void dq_chunk(uint32_t kb, int gr, int gp, int i, half2_t dd, const GSet<ROPE> &G) {
+    const half2_t d = i < 2 ? __builtin_shufflevector(dd, dd, 0, 0) : __builtin_shufflevector(dd, dd, 1, 1);
+    const uint32_t wv = G.c[i];
+    u32x4_t v;
+    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 0) * d);
+    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 1) * d);
+    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 2) * d);
+    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 3) * d);
+    lds_st<u32x4_t>(kb + kswz(gr, 4 * gp + i), v);
+}
+template <bool ROPE>
+__device__ __forceinline__ void dq_rope(uint32_t kb, int gr, int gp, const GSet<ROPE> &G) {
+    const u32x2_t rp = G.valid ? G.rp : u32x2_t{0, 0};
+    u32x4_t h;
+    h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, false));
+    h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, true));
+    h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, false));
+    h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, true));
+    lds_st<u32x4_t>(kb + kswz(gr, 64 + gp), h);
+}
+
 // rope_part: this wavefront stores the rope chunk (wave-uniform: wavefronts 0..3)
 template <bool ROPE>
 __device__ __forceinline__ void dequant_set(uint32_t kb, int gr, int gp, bool rope_part, const GSet<ROPE> &G) {
-    const uint32_t sc = G.valid ? G.sc >> (16 * (gp & 1)) : 0u;                     // this part's two scales
-    const half2_t dd = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);   // E4M3 -> fp16, exact
-    const half2_t d0 = __builtin_shufflevector(dd, dd, 0, 0), d1 = __builtin_shufflevector(dd, dd, 1, 1);
+    const half2_t dd = dq_scales<ROPE>(G, gp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {             // chunk 4gp + i: dims 32gp + 8i .. +7, block 2gp + i / 2
-        const uint32_t wv = G.c[i];
-        const half2_t d = i < 2 ? d0 : d1;
-        u32x4_t v;
-        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 0) * d);
-        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 1) * d);
-        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 2) * d);
-        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv, 1.0f, 3) * d);
-        lds_st<u32x4_t>(kb + kswz(gr, 4 * gp + i), v);
-    }
+    for (int i = 0; i < 4; ++i) dq_chunk<ROPE>(kb, gr, gp, i, dd, G);
     if constexpr (ROPE) {
-        if (rope_part) {
-            const u32x2_t rp = G.valid ? G.rp : u32x2_t{0, 0};
-            u32x4_t h;
-            h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, false));
-            h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[0], 1.0f, true));
-            h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, false));
-            h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rp[1], 1.0f, true));
-            lds_st<u32x4_t>(kb + kswz(gr, 64 + gp), h);
-        }
+        if (rope_part) dq_rope<ROPE>(kb, gr, gp, G);
     }
 }
 
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     float *row_sum = reinterpret_cast<float *>(lds + kOffRowSum);   // [head group][half][head]: the halves' l
     float *row_ref = reinterpret_cast<float *>(lds + kOffRowRef);   // [head group][head]: the reference m_ref
     int32_t *flag = reinterpret_cast<int32_t *>(lds + kOffFlag);
-    const uint32_t L = lds_addr(lds);
+    const uint32_t L = lds_addr(lds) + kOffK;      // base of the K tiles and the areas sharing their space
 
     // wavefront-uniform values live in scalar registers, so the branches on
     // them are scalar and no lane mask is ever saved and restored
@@ -940,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     float *row_sum = reinterpret_cast<float *>(lds + kOffRowSum);   // [hg][rh][head]: the row halves' l
     float *row_ref = reinterpret_cast<float *>(lds + kOffRowRef);   // [hg][head]: the reference m_ref
     int32_t *flag = reinterpret_cast<int32_t *>(lds + kOffFlag);
-    const uint32_t L = lds_addr(lds);
+    const uint32_t L = lds_addr(lds) + kOffK;      // base of the K tiles and the areas sharing their space
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1055,19 +1073,27 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         stage_q();
         __syncthreads();                           // every head row staged
 
+        // k-step ks of lane group q4 covers chunk C(ks, q4) = 8 (ks / 2) +
+        // 2 (ks % 2) + cq, cq = q4 / 2 + 4 (q4 % 2): the two 16-lane groups of
+        // a half-wavefront then read chunks 4 apart, whose rows the K-tile
+        // layout permutes alike, which a ds_read_b128 needs to be free of bank
+        // conflicts (groups with different permutations in one half-wavefront
+        // conflict two-way).  Any assignment of dims to (ks, q4) gives the same
+        // scores as long as queries and keys share it.
+        const int cq = (q4 >> 1) + 4 * (q4 & 1);
         // queries: B operand of S^T = K Q^T.  Lane (l16, q4) holds head h0 +
-        // 32 hg + 16 hb + l16, dims 32 ks + 8 q4 .. +7.  The power-of-two scale
+        // 32 hg + 16 hb + l16, dims 8 C(ks, q4) .. +7.  The power-of-two scale
         // qs puts the head's largest |q| in [2^13, 2^14), exact in fp16;
         // score_mul = sm_scale log2(e) / qs turns scores into log2 units.
         half8_t qb[2][kKs];
         float score_mul[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-            const uint32_t qf = Lq + (32 * hg + 16 * hb + l16) * kQRow + 16 * q4;
+            const uint32_t qf = Lq + (32 * hg + 16 * hb + l16) * kQRow + 16 * cq;
             float qmax = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) {     // read twice (maximum, conversion): fewer live registers
-                const u32x4_t v = lds_ld<u32x4_t>(qf + 64 * ks);
+                const u32x4_t v = lds_ld<u32x4_t>(qf + 128 * (ks >> 1) + 32 * (ks & 1));
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[c] << 16)),
@@ -1079,9 +1105,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
             if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
             const float qs = __builtin_ldexpf(1.0f, 14 - ex);
             score_mul[hb] = p.score_mul / qs;
+            asm volatile("" ::: "memory");         // read again: the first pass's values are not kept
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) {
-                const u32x4_t v = lds_ld<u32x4_t>(qf + 64 * ks);
+                const u32x4_t v = lds_ld<u32x4_t>(qf + 128 * (ks >> 1) + 32 * (ks & 1));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     qb[hb][ks][2 * c] = (_Float16)(__uint_as_float(v[c] << 16) * qs);
@@ -1090,8 +1117,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
             }
         }
 
-        // score operand (A of 16x16x32): row 16 rh + l16, chunk 4 ks + q4
-        const uint32_t a_off = q4 * kChunkB + 16 * ((16 * rh + l16) ^ (4 * q4));
+        // score operand (A of 16x16x32): row 16 rh + l16, chunk C(ks, q4), at
+        // a_off[ks % 2] + 8 kChunkB (ks / 2) (C % 4 = 2 (ks % 2) + q4 / 2)
+        const uint32_t a_off0 = cq * kChunkB + 16 * ((16 * rh + l16) ^ (4 * (q4 >> 1)));
+        const uint32_t a_off1 = (cq + 2) * kChunkB + 16 * ((16 * rh + l16) ^ (4 * (2 + (q4 >> 1))));
         // P of head 32 hg + 16 hb + l16, rows 16 rh + 4 q4 + 0..3: 8 contiguous
         // bytes in the P.V operand order (row bits 2 and 3 swapped)
         const uint32_t px_w = L + kOffP2 + (32 * hg + l16) * kPXHead + 2 * (16 * rh + 8 * (q4 & 1) + 4 * (q4 >> 1));
@@ -1103,10 +1132,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         bool need_redo = false;
 
         auto scores = [&](uint32_t kb, floatx4_t (&acc)[2]) {
-            const uint32_t a0 = kb + a_off;
+            const uint32_t a0 = kb + a_off0, a1 = kb + a_off1;
+            auto a_at = [&](int ks) { return (ks & 1 ? a1 : a0) + 8 * kChunkB * (ks >> 1); };
             half8_t a[kAhead];
 #pragma unroll
-            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>(a0 + 4 * kChunkB * i);
+            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>(a_at(i));
             __builtin_amdgcn_sched_barrier(0);
             acc[0] = floatx4_t{0, 0, 0, 0};
             acc[1] = floatx4_t{0, 0, 0, 0};
@@ -1115,9 +1145,37 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 const half8_t cur = a[ks % kAhead];
                 acc[0] = mfma16(cur, qb[0][ks], acc[0]);
                 acc[1] = mfma16(cur, qb[1][ks], acc[1]);
-                if (ks + kAhead < kKs) a[ks % kAhead] = lds_ld<half8_t>(a0 + 4 * kChunkB * (ks + kAhead));
+                if (ks + kAhead < kKs) a[ks % kAhead] = lds_ld<half8_t>(a_at(ks + kAhead));
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        // the same, with the dequantization of set G into the K tile at kd laid
+        // between the first MFMAs (an in-order wavefront then issues its
+        // conversions and stores while the matrix pipe works) and, once G is
+        // consumed, the gather of slot `next` into it: as early in the phase
+        // as possible, for the longest time in flight
+        auto scores_dq = [&](uint32_t kb, floatx4_t (&acc)[2], uint32_t kd, GSet<ROPE> &G, int32_t next) {
+            const uint32_t a0 = kb + a_off0, a1 = kb + a_off1;
+            auto a_at = [&](int ks) { return (ks & 1 ? a1 : a0) + 8 * kChunkB * (ks >> 1); };
+            half8_t a[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) a[i] = lds_ld<half8_t>(a_at(i));
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] = floatx4_t{0, 0, 0, 0};
+            acc[1] = floatx4_t{0, 0, 0, 0};
+            half2_t dd;
+            static_for<0, kKs>([&](auto slot) {
+                constexpr int ks = decltype(slot)::value;
+                const half8_t cur = a[ks % kAhead];
+                acc[0] = mfma16(cur, qb[0][ks], acc[0]);
+                acc[1] = mfma16(cur, qb[1][ks], acc[1]);
+                if constexpr (ks + kAhead < kKs) a[ks % kAhead] = lds_ld<half8_t>(a_at(ks + kAhead));
+                if constexpr (ks == 0) dd = dq_scales<ROPE>(G, gp);
+                if constexpr (ks >= 1 && ks <= 4) dq_chunk<ROPE>(kd, gr, gp, ks - 1, dd, G);
+                if constexpr (ROPE && ks == 5) dq_rope<ROPE>(kd, gr, gp, G);
+                if constexpr (ks == 6) gather_set<ROPE>(p.pool, stand_in, next, gp, G);
+                __builtin_amdgcn_sched_barrier(0);
+            });
         };
         // P = 2^(s - m_ref) of this lane's 4 rows x 2 heads into P buffer pb;
         // rows >= lim are padding
@@ -1149,18 +1207,20 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 lds_st<half4_t>(px_w + pb * kPXB + hb * (16 * kPXHead), ph);
             }
         };
-        // phase: scores and softmax of t + 1, dequantization of t + 2 (latent
-        // dims 0..255 and the rope), gather of t + 4 (clamped to the chunk's
-        // last tile: a harmless repeat that keeps the loads unconditional)
+        // phase: scores and softmax of t + 1, with the dequantization of t + 2
+        // (latent dims 0..255 and the rope) and the gather of t + 4 (clamped
+        // to the chunk's last tile: a harmless repeat) inside the scores; the
+        // last phase of a chunk has no scores and needs neither
         auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bB, uint32_t bC) {
             const int32_t next = slots[min(t + 4, n_t - 1) * kTile + gr];
             if (t + 1 < n_t) {
+                // the dequantization runs whether tile t + 2 exists or not:
+                // bC's last reader was the P.V of t - 1, and a set past the
+                // chunk holds a repeat of its last tile
                 floatx4_t acc[2];
-                scores(bB, acc);
+                scores_dq(bB, acc, bC, G, next);
                 softmax(acc, tile_lim(t + 1), (t + 1) & 1);
             }
-            if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, true, G);
-            gather_set<ROPE>(p.pool, stand_in, next, gp, G);
             __syncthreads();
         };
 
@@ -1262,7 +1322,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         const uint32_t px_r = L + kOffP2 + l32 * kPXHead + 2 * (8 * g);
         floatx16_t o[4][2];
 
-        auto pv = [&](uint32_t kb, int pb) {
+        auto pv = [&](uint32_t kb, int pb, uint32_t kd, GSet<ROPE> &G, int next_tile) {
             const uint32_t t0 = kb + tr_off0, t1 = kb + tr_off1;
             half8_t pbv[2][2];
 #pragma unroll
@@ -1279,23 +1339,26 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
 #pragma unroll
             for (int j = 0; j < kTrAhead; ++j) issue(j);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int md = j & 3, kk = j >> 2;
+            half2_t dd;
+            static_for<0, 8>([&](auto step) {
+                constexpr int j = decltype(step)::value;
+                constexpr int md = j & 3, kk = j >> 2;
                 const half8_t a = __builtin_bit_cast(
                     half8_t, __builtin_shufflevector(lo[j % kTrAhead], hi[j % kTrAhead], 0, 1, 2, 3, 4, 5, 6, 7));
                 o[md][0] = mfma32(a, pbv[0][kk], o[md][0]);
                 o[md][1] = mfma32(a, pbv[1][kk], o[md][1]);
-                if (j + kTrAhead < 8) issue(j + kTrAhead);
+                if constexpr (j + kTrAhead < 8) issue(j + kTrAhead);
+                if constexpr (j == 0) dd = dq_scales<ROPE>(G, gp);
+                if constexpr (j >= 1 && j <= 4) dq_chunk<ROPE>(kd, gr, gp, j - 1, dd, G);   // between the MFMAs
+                if constexpr (j == 5) gather_units(next_tile, G);                         // G consumed: refill
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         };
-        // phase: P.V of t, dequantization of t + 2 (latent dims 256..511),
-        // gather of t + 4
+        // phase: P.V of t with the dequantization of t + 2 (latent dims
+        // 256..511; it runs whether t + 2 exists or not, as on the score
+        // side) and then the gather of t + 4 between its MFMAs
         auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bA, uint32_t bC) {
-            pv(bA, t & 1);
-            if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, false, G);
-            gather_units(min(t + 4, n_t - 1), G);
+            pv(bA, t & 1, bC, G, min(t + 4, n_t - 1));
             __syncthreads();
         };
 
@@ -1339,18 +1402,23 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         if (err && p.err_word) atomicOr(p.err_word, err);
         // O = O_acc / l staged for the coalesced store (row sums and the
         // reference were written before the passes' last barrier)
+        // the lane index read afresh (not derived from values kept through
+        // the loop, which would hold registers there)
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int el32 = ln & 31, eg = ln >> 5;
         auto stage = [&](auto half_out) {
             constexpr bool kH = decltype(half_out)::value;
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
-                const float l_tot = row_sum[(hb * 2) * 32 + l32] + row_sum[(hb * 2 + 1) * 32 + l32];
+                const float l_tot = row_sum[(hb * 2) * 32 + el32] + row_sum[(hb * 2 + 1) * 32 + el32];
                 const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-                const uint32_t row = L + (32 * hb + l32) * (kH ? kORowH : kORowF);
+                const uint32_t row = L + (32 * hb + el32) * (kH ? kORowH : kORowF);
 #pragma unroll
                 for (int md = 0; md < 4; ++md)
 #pragma unroll
                     for (int vq = 0; vq < 4; ++vq) {
-                        const int dim = 128 * dq + 32 * md + 8 * vq + 4 * g;
+                        const int dim = 128 * dq + 32 * md + 8 * vq + 4 * eg;
                         const floatx4_t v = floatx4_t{o[md][hb][4 * vq], o[md][hb][4 * vq + 1], o[md][hb][4 * vq + 2],
                                                       o[md][hb][4 * vq + 3]} * inv;
                         if constexpr (kH) lds_st<half4_t>(row + 2 * dim, __builtin_convertvector(v, half4_t));
