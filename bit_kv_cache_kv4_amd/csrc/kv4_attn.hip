@@ -10,42 +10,42 @@
 // gathered once per task.
 //
 // Workgroup = 8 wavefronts, two per SIMD, for one task (query row r, split s,
-// chunk of up to 64 heads), in two roles:
-//  - score wavefronts 0..3 = (head group hg = w % 2 of 32 heads, half = w / 2):
-//    the queries of 32 heads over half the dims in registers; per tile the
-//    partial scores S^T[32 rows x 32 heads] over those dims
-//    (v_mfma_f32_32x32x16_f16), swapped with the partner half through LDS so
-//    each owns 16 rows, and the softmax of those rows;
-//  - P.V wavefronts 4..7 = quarter dq of the 512 latent dims: O^T[128 dims x 64
-//    heads] accumulated from V^T (read from the same K tile through
-//    ds_read_b64_tr_b16) and the P of all 64 heads (LDS).
-// A SIMD holds one wavefront of each role, so per tile it issues 18 score and
-// 16 P.V MFMAs.  The roles exist because LDS bandwidth, not the MFMA pipe,
-// bounds this loop on gfx950 (stores about 78 B/clk per CU, plain reads about
-// 195 and transposing reads about 92 measured): keeping the queries and the
-// accumulators in different wavefronts lets each V^T and P element be read once
-// per tile and the score partials be split two ways only, for about 48 KB
-// written and 128 KB read per tile instead of 64 and 176.  The two roles run
-// their own loops, so each wavefront's registers hold only its role's state,
-// and they meet at the same barriers.
-// Per tile t, with three K tiles in rotation:
-//   phase 1: softmax of t (P to LDS) and scores of t + 1 (score wavefronts);
-//            dequantization of tile t + 2, latent dims 256..511 (P.V wavefronts)
-//   phase 2: P.V of t (P.V wavefronts); the partial-score swap of t + 1 and the
-//            dequantization of t + 2, latent dims 0..255 and the rope (score
-//            wavefronts)
-// with one barrier after each phase.  Gathering: the entries' pool slots
-// (translated once per chunk of 2048 entries, valid ones packed to the front,
-// kept in LDS) name 32 rows; thread t loads row t % 32, part t / 32 (32 latent
-// dims, their 2 block scales, 8 rope dims) four tiles ahead of its use, and
-// dequantizes with gfx950's FP4/FP8 -> fp16 conversions at scale 1 and one
-// packed multiply by the E4M3 block scale (every product is exact in fp16).
+// chunk of up to 64 heads), in two roles that run their own loops (so each
+// wavefront's registers hold only its role's state) and meet at the same
+// barriers: score wavefronts 0..3 (queries in registers, scores, softmax, P
+// into LDS) and P.V wavefronts 4..7 (quarter dq of the 512 latent dims:
+// O^T[128 dims x 64 heads] accumulated from V^T, read from the K tile itself
+// through ds_read_b64_tr_b16, and the P of all 64 heads).  A SIMD holds one
+// wavefront of each role.  LDS bandwidth bounds these loops on gfx950 as much
+// as the MFMA pipe (stores about 78 B/clk per CU, plain reads about 195 and
+// transposing reads about 92, measured); the roles let each V^T and P element
+// be read once per tile.
+//
+// bf16 queries (sparse_mla_bf16_kernel): score wavefront = (head group hg =
+// w % 2 of 32 heads, row half rh = w / 2 of each tile) holds its heads' queries
+// over all dims and computes whole scores S^T[16 rows x 32 heads]
+// (v_mfma_f32_16x16x32_f16), so no partial scores are swapped and a tile takes
+// one barrier: scores and softmax of t + 1 beside the P.V of t, both roles
+// dequantizing t + 2 between their MFMAs.  fp32 queries (split into hi and lo
+// fp16 parts: twice the registers, sparse_mla_f32q_kernel): score wavefront =
+// (head group, half of the dims), partial scores S^T[32 rows x 32 heads]
+// (v_mfma_f32_32x32x16_f16) swapped with the partner half through LDS so each
+// owns 16 rows; two phases per tile (softmax of t and scores of t + 1, then
+// the swap beside the P.V of t), the P.V wavefronts dequantizing whole rows.
+//
+// Gathering: the entries' pool slots (translated once per chunk of 2048
+// entries, valid ones packed to the front, kept in LDS) name 32 rows; thread
+// t loads row t % 32, part t / 32 (32 latent dims, their 2 block scales, 8
+// rope dims) four tiles ahead of its use, and dequantizes with gfx950's
+// FP4/FP8 -> fp16 conversions at scale 1 and one packed multiply by the E4M3
+// block scale (every product is exact in fp16; the conversions' own scale
+// operand applies only its power of two).  Three K tiles rotate.
 // The softmax uses P = 2^(s - m_ref) with m_ref the head's largest score in
-// the first tile (agreed across the two halves); if a later score exceeds
-// m_ref + 15 (P could overflow fp16) the workgroup runs the list again with
-// m_ref = the exact maximum, which the first pass tracked.  The per-split
-// result is written normalised with its lse; a split count of 1 writes the
-// final output.
+// the first tile (agreed across the wavefronts sharing the head); if a later
+// score exceeds m_ref + 15 (P could overflow fp16) the workgroup runs the list
+// again with m_ref = the exact maximum, which the first pass tracked.  The
+// per-split result is written normalised with its lse; a split count of 1
+// writes the final output.
 //
 // Rows are either the 352-byte format (576 dims: 512 latent + 64 rope) or the
 // 288-byte rope-free format (512 latent dims; README, "4-bit KV cache": the
@@ -289,15 +289,15 @@ __device__ __forceinline__ void dequant_set(uint32_t kb, int gr, int gp, bool ro
 
 }  // namespace
 
-template <bool QF32, bool ROPE>
-__global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
+template <bool ROPE>
+__global__ __launch_bounds__(kThreads) void sparse_mla_f32q_kernel(AttnParams p) {
     // K has kD dims (latent + rope, or latent only); a score wavefront's half
     // of them is kHd dims = kKs MFMA k-steps of 16 = kHc chunks of 8
     constexpr int kD = ROPE ? kDim : kLatent;
     constexpr int kHd = kD / 2;
     constexpr int kKs = kHd / 16;
     constexpr int kHc = kHd / 8;
-    constexpr int kAhead = QF32 ? 2 : 4;       // score operands read ahead of their MFMA
+    constexpr int kAhead = 2;                  // score operands read ahead of their MFMA
     constexpr int kTrAhead = 4;                // P.V operand pairs read ahead
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     int32_t *slots = reinterpret_cast<int32_t *>(lds + kOffSlots);
@@ -334,19 +334,17 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     // up the page-table loads), the slots packed, the first gathers issued,
     // and only then the queries staged in LDS (rows padded so the fragment
     // reads are conflict-free).
-    // All 64 head rows are staged at once: bf16 ones in the third K tile and
-    // the exchange areas (free until the first tile's scores), so the first
-    // two tiles can be dequantized while the score wavefronts still read the
-    // queries; fp32 ones fill most of the LDS (the slot list lies beyond), and
-    // a barrier separates their last read from the first K-tile store.
-    constexpr int kQE = QF32 ? 4 : 2;                      // bytes per query element
+    // All 64 fp32 head rows are staged at once; they fill most of the LDS
+    // (the slot list lies beyond), and a barrier separates their last read
+    // from the first K-tile store.
+    constexpr int kQE = 4;                                 // bytes per query element
     constexpr int kQRow = kD * kQE + 16;                   // staged head row
     constexpr int kQH = 64;                                // heads staged
-    const uint32_t Lq = QF32 ? L : L + 2 * kKTileB;        // staging base
+    const uint32_t Lq = L;                                 // staging base
     constexpr int kQChunks = kD * kQE / 16;                // 16-byte chunks per head row
     constexpr int kQPer = kQH * kQChunks / kThreads;       // chunks per thread
     static_assert(kQH * kQChunks % kThreads == 0, "query chunks do not divide");
-    static_assert(kQH * kQRow <= (QF32 ? kStageBytes : kStageBytes - 2 * kKTileB), "staged queries overlap the slot list");
+    static_assert(kQH * kQRow <= kStageBytes, "staged queries overlap the slot list");
     // thread t loads head t / kTPH, 16-byte chunks t % kTPH +
     // kTPH i: one base address per thread, consecutive threads on consecutive
     // chunks of a head row
@@ -373,20 +371,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     const int first_hi = min(e_hi, e_lo + kSlotCap);
     load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
     u32x4_t qc[kQPer];
-    if constexpr (QF32) {
-        // fp32 rows (147 KB) are staged before the roles split: their 72
-        // registers per thread must not stay live into the roles
-        load_q(qc);
-        load_pages(p, lc, pos, phys);
-        stage_q(qc);
-    } else {
-        load_pages(p, lc, pos, phys);
-        load_q(qc);                                // after the page-table loads: it must not delay them
-    }
+    // the rows (147 KB) are staged before the roles split: their 72 registers
+    // per thread must not stay live into the roles
+    load_q(qc);
+    load_pages(p, lc, pos, phys);
+    stage_q(qc);
     int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
     if (tid == 0) *flag = 0;
-    __syncthreads();                               // slots[] complete; with bf16 queries each role issues
-                                                   // its first gathers, then stages its queries
+    __syncthreads();                               // slots[] complete, queries staged
 
     const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
     int n_t = 0, n_real = 0, last_rows = kTile;   // tiles (even), tiles holding entries, rows of the last
@@ -440,28 +432,18 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     if (w < 4) {
         // ================================================ score wavefronts
         const int hg = w & 1, half = w >> 1;
-        // parts 0..7 of a tile's rows, with the rope (for fp32 queries, whose
-        // registers these wavefronts need, the P.V wavefronts take them)
-        constexpr bool kDq = !QF32;
-        GSet<ROPE> G0, G1;
-        if (kDq && nv > 0) {                       // tile 1 exists: chunks have an even number of tiles
-            gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
-            gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
-        }
-        if constexpr (!QF32) {
-            stage_q(qc);
-            __syncthreads();                       // every head row staged
-        }
+        // (the queries' registers leave no room for gathers here: the P.V
+        // wavefronts gather and dequantize whole rows)
 
         // queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head h0 +
         // 32hg + l32, dims kHd half + 16 ks + 8 g .. +7 for ks < kKs.  The
         // power-of-two scale qs puts the largest |q| of the head's half in
-        // [2^13, 2^14): exact in fp16 for bf16 queries; fp32 queries get a hi
-        // and a lo fp16 part.  Each half has its own scale: its partial scores
+        // [2^13, 2^14); each fp32 query becomes a hi and a lo fp16 part (two
+        // MFMAs per k-step).  Each half has its own scale: its partial scores
         // are multiplied by score_mul = sm_scale log2(e) / qs before the two
         // halves are added, so no exchange between them is needed here.
         half8_t qb[kKs];
-        half8_t ql[QF32 ? kKs : 1];
+        half8_t ql[kKs];
         float score_mul = 0.0f;
         {
             const uint32_t qf = Lq + (32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
@@ -473,53 +455,32 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                 score_mul = p.score_mul / qs;
                 return qs;
             };
-            if constexpr (QF32) {
-                // read twice, for the maximum and for the conversion, so the
-                // fp32 fragment never occupies registers beside its fp16 form
-                float qmax = 0.0f;
+            // read twice, for the maximum and for the conversion, so the
+            // fp32 fragment never occupies registers beside its fp16 form
+            float qmax = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks)
+            for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
-                        qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                                                                     __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
-                    }
-                const float qs = scale_of(qmax);
-#pragma unroll
-                for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float x = v[e] * qs;
-                            const _Float16 hi = (_Float16)x;
-                            qb[ks][4 * j + e] = hi;
-                            ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
-                        }
-                    }
-                __syncthreads();                   // the first K tiles overwrite the staged queries
-            } else {
-                u32x4_t v[kKs];
-                float qmax = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    v[ks] = lds_ld<u32x4_t>(qf + 32 * ks);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[ks][c] << 16)),
-                                                                     __builtin_fabsf(__uint_as_float(v[ks][c] & 0xFFFF0000u))));
+                for (int j = 0; j < 2; ++j) {
+                    const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                                 __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
                 }
-                const float qs = scale_of(qmax);
+            const float qs = scale_of(qmax);
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks)
+            for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        qb[ks][2 * c] = (_Float16)(__uint_as_float(v[ks][c] << 16) * qs);
-                        qb[ks][2 * c + 1] = (_Float16)(__uint_as_float(v[ks][c] & 0xFFFF0000u) * qs);
+                for (int j = 0; j < 2; ++j) {
+                    const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = v[e] * qs;
+                        const _Float16 hi = (_Float16)x;
+                        qb[ks][4 * j + e] = hi;
+                        ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
                     }
-            }
+                }
+            __syncthreads();                   // the first K tiles overwrite the staged queries
         }
 
         // score operand (A of S^T = K Q^T): row l32, chunk kHc half + 2 ks + g;
@@ -557,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             for (int ks = 0; ks < kKs; ++ks) {
                 const half8_t cur = a[ks % kAhead];
                 acc = mfma32(cur, qb[ks], acc);
-                if constexpr (QF32) acc = mfma32(cur, ql[ks], acc);
+                acc = mfma32(cur, ql[ks], acc);
                 if (ks + kAhead < kKs) {
                     const int n = ks + kAhead;
                     a[ks % kAhead] = lds_ld<half8_t>((n & 1 ? a1 : a0) + 2 * kChunkB * n);
@@ -638,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                 constexpr int ks = decltype(slot)::value;
                 const half8_t cur = a[ks % kAhead];
                 acc = mfma32(cur, qb[ks], acc);
-                if constexpr (QF32) acc = mfma32(cur, ql[ks], acc);
+                acc = mfma32(cur, ql[ks], acc);
                 if constexpr (ks + kAhead < kKs)
                     a[ks % kAhead] = lds_ld<half8_t>(((ks + kAhead) & 1 ? a1 : a0) + 2 * kChunkB * (ks + kAhead));
                 if constexpr (ks == 2)
@@ -689,19 +650,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             sacc = acc;
         };
         // phase 1: softmax of t, scores of t + 1; phase 2: the swap of t + 1's
-        // partials, dequantization of t + 2 (latent dims 0..255 and the rope)
-        // and the gather of t + 4 (a tile index past the chunk is clamped to
-        // its last tile: a harmless repeat that keeps the loads unconditional)
-        auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bB, uint32_t bC) {
-            const int32_t next = slots[min(t + 4, n_t - 1) * kTile + gr];
+        // partials (the P.V wavefronts dequantize and gather whole rows)
+        auto iteration = [&](int t, uint32_t bB) {
             if (t + 1 < n_t) scores_softmax(bB, tile_lim(t));
             else softmax(tile_lim(t), lds_ld<floatx4_t>(x_r), lds_ld<floatx4_t>(x_r + 16));
             __syncthreads();
             if (t + 1 < n_t) exchange();
-            if constexpr (kDq) {
-                if (t + 2 < n_t) dequant_set<ROPE>(bC, gr, gp, true, G);
-                gather_set<ROPE>(p.pool, stand_in, next, gp, G);
-            }
             __syncthreads();
         };
 
@@ -712,17 +666,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                 if (c_lo != e_lo || (pass == 1 && e_hi - e_lo > kSlotCap)) fresh_chunk(c_lo, c_hi);
                 chunk_tiles();
                 if (n_real == 0) continue;         // nothing valid in this chunk (uniform)
-                // tiles 0 and 1 into K0 and K1, tiles 2 and 3 in flight, scores of tile 0
-                if constexpr (kDq) {
-                    if (pass == 1 || c_lo != e_lo) {   // the first chunk's were gathered before the passes
-                        gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
-                        gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
-                    }
-                    dequant_set<ROPE>(K0, gr, gp, true, G0);
-                    gather_set<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, G0);
-                    dequant_set<ROPE>(K1, gr, gp, true, G1);
-                    gather_set<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, G1);
-                }
                 __syncthreads();                   // tiles 0 and 1 in LDS
                 scores(K0);
                 exchange();
@@ -743,8 +686,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
                 }
                 uint32_t bA = K0, bB = K1, bC = K2;
                 for (int t = 0; t < n_t; t += 2) {
-                    iteration(t, G0, bB, bC);      // G0: tile t + 2 -> bC, then t + 4
-                    iteration(t + 1, G1, bC, bA);  // G1: tile t + 3 -> bA, then t + 5
+                    iteration(t, bB);
+                    iteration(t + 1, bC);
                     const uint32_t a0 = bA;        // tiles t + 2, t + 3, t + 4 go to bC, bA, bB
                     bA = bC;
                     bC = bB;
@@ -772,9 +715,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
     } else {
         // ================================================ P.V wavefronts
         const int dq = w - 4;
-        // parts 8..15 of a tile's rows, no rope; with fp32 queries also parts
-        // 0..7 with the rope (unit 1)
-        constexpr int kUnits = QF32 ? 2 : 1;
+        // parts 8..15 of a tile's rows, no rope (unit 0), and parts 0..7 with
+        // the rope (unit 1)
+        constexpr int kUnits = 2;
         GSet<ROPE> G0[kUnits], G1[kUnits];
         auto gather_units = [&](int tile, GSet<ROPE> (&G)[kUnits]) {
             const int32_t slot = slots[tile * kTile + gr];
@@ -789,12 +732,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(AttnParams p) {
             gather_units(0, G0);
             gather_units(1, G1);
         }
-        if constexpr (!QF32) {
-            stage_q(qc);
-            __syncthreads();                       // every head row staged
-        } else {
-            __syncthreads();                       // the score wavefronts have read the staged queries
-        }
+        __syncthreads();                           // the score wavefronts have read the staged queries
         // transposing reads (A of O^T = V^T P^T): this lane names row j4 + 4g
         // (+8 for the second read of a k-step, +16 for the second k-step), 8
         // bytes at latent dims 128 dq + 32 md + 8 cc + 4 (lane & 1) .. +3, so
@@ -1447,10 +1385,10 @@ hipError_t launch_sparse_mla(const AttnParams &p, bool q_f32, int32_t n_splits, 
     if (p.n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)p.n_rows, (unsigned)n_splits, (unsigned)((p.n_heads + 63) / 64));
     if (p.rope_dims == kRope) {
-        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(kThreads), 0, stream, p);
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_f32q_kernel<true>), grid, dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL((sparse_mla_bf16_kernel<true>), grid, dim3(kThreads), 0, stream, p);
     } else {
-        if (q_f32) hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
+        if (q_f32) hipLaunchKernelGGL((sparse_mla_f32q_kernel<false>), grid, dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL((sparse_mla_bf16_kernel<false>), grid, dim3(kThreads), 0, stream, p);
     }
     return hipGetLastError();

@@ -57,7 +57,7 @@ def test_every_kernel_is_spill_free(resources):
 
 
 def test_attention_keeps_two_wavefronts_per_simd(resources):
-    attn = {k: v for k, v in resources.items() if "sparse_mla_kernel" in k or "sparse_mla_bf16_kernel" in k}
+    attn = {k: v for k, v in resources.items() if "sparse_mla_f32q_kernel" in k or "sparse_mla_bf16_kernel" in k}
     assert len(attn) == 4                                   # {bf16, fp32 queries} x {352, 288-byte rows}
     for k, v in attn.items():
         assert int(v["Occupancy [waves/SIMD]"]) >= 2, (k, v)
