@@ -12,7 +12,9 @@ keep the gathered rows from being served out of the 256 MB Infinity Cache.
 
 Prints one JSON line: decode tokens/s (value), the roofline of the dominant
 kernel (the per-split decode kernel, timed with HIP events on the stream it
-runs on), prefill MFMA utilisation, and the CPU oracle on the host's cores.
+runs on), prefill MFMA utilisation, and the CPU oracle on the host's cores
+(the decode step above, then each other config's unit of work, with 1-thread
+runs of the tiny decode and the write + compaction).
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-CPU_BASELINE_SECONDS = 10.0
+CPU_BASELINE_SECONDS = 6.0     # oracle decode steps timed; the other configs get shorter budgets
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 N_SETS = 8                     # rotating list/query sets
@@ -166,12 +168,41 @@ def traffic_from_profiles(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def _time_oracle(fn, budget_s, min_reps=1):
+    """Repeat fn until budget_s seconds of it are timed (at least min_reps
+    runs); returns (runs, seconds)."""
+    reps, dt = 0, 0.0
+    while reps < min_reps or dt < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        dt += time.perf_counter() - t0
+        reps += 1
+    return reps, dt
+
+
+def _decode_inputs_host(spec, dev):
+    """Host inputs of one decode call of a DecodeSpec for the oracle: fp32
+    queries, the lists rewritten to index a pool of the rows they select
+    (quantized by the oracle from the same fp32 originals as the device pool)."""
+    import oracle
+    import workloads as W
+    pt_h, topk_h = W.page_table(spec), W.topk_lists(spec)
+    uniq, rows, slots = gathered_rows_host(spec, pt_h, topk_h, dev)
+    pool_h = np.zeros((uniq.size, 352), dtype=np.uint8)
+    oracle.quant_write(rows, np.arange(uniq.size, dtype=np.int32), pool_h)
+    compact = np.searchsorted(uniq, slots).astype(np.int32)
+    q = W.queries(spec).float().numpy()
+    return q, pool_h, compact
+
+
 def run_cpu_baseline(spec, wl, dev):
     """The oracle, as it is, on the host cores: the same decode step (write
     the requests' new rows, dedup their lists, attention) for every request
     of one rotating set, over a host pool of the selected rows that the
-    oracle quantized itself (untimed setup)."""
+    oracle quantized itself (untimed setup); then the other configs' units of
+    work (per_config), with 1-thread runs of C1 and C4."""
     import oracle
+    import workloads as W
     st = wl["sets"][0]
     uniq, rows, slots = gathered_rows_host(spec, wl["pt_h"], st["topk_h"], dev)
     pool_h = np.zeros((uniq.size + spec.n_req, 352), dtype=np.uint8)
@@ -181,19 +212,88 @@ def run_cpu_baseline(spec, wl, dev):
     new_rows = st["new_rows"].cpu().numpy()
     new_slots = np.arange(uniq.size, uniq.size + spec.n_req, dtype=np.int32)
     threads = oracle.num_threads()
-    steps, dt = 0, 0.0
-    while dt < CPU_BASELINE_SECONDS:          # the same step again until about 10 s of work is timed
-        t0 = time.perf_counter()
+    affinity = len(os.sched_getaffinity(0))
+
+    def step():
         oracle.quant_write(new_rows, new_slots, pool_h)
         lists, _ = oracle.dedup_compact(compact)
         oracle.sparse_mla(q, pool_h, lists, spec.sm_scale)
-        dt += time.perf_counter() - t0
-        steps += 1
-    return {"value": spec.n_req * steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d repetitions of one full decode step of %s: %d requests (write %d new rows, dedup %d lists "
-                      "of %d, attention %d heads x %d keys each), host pool of the %d selected rows; %.2f s wall on %d "
-                      "threads" % (steps, spec.name, spec.n_req, spec.n_req, spec.n_req, spec.k, spec.n_heads, spec.k,
-                                   uniq.size, dt, threads)}
+
+    steps, dt = _time_oracle(step, CPU_BASELINE_SECONDS)
+    res = {"value": spec.n_req * steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "affinity_cores": affinity,
+           "sample": "%d repetitions of one full decode step of %s: %d requests (write %d new rows, dedup %d lists "
+                     "of %d, attention %d heads x %d keys each), host pool of the %d selected rows; %.2f s wall on %d "
+                     "threads" % (steps, spec.name, spec.n_req, spec.n_req, spec.n_req, spec.k, spec.n_heads, spec.k,
+                                  uniq.size, dt, threads)}
+    print("[bench] cpu baseline: other configs", file=sys.stderr, flush=True)
+    res["per_config"] = run_cpu_baseline_configs(dev, threads)
+    return res
+
+
+def run_cpu_baseline_configs(dev, threads):
+    """Oracle time per unit of each config's GPU measurement: a decode call
+    for C1 and C2 (attention of every request), the write of 16,384 tokens and
+    the dedup of 4096 lists for C4, and prefill rows for C5 (a stated subset of
+    the 4096 rows, extrapolated).  C1 and C4 also on one thread."""
+    import oracle
+    import workloads as W
+    out = {}
+
+    def with_threads(n, fn):
+        old = oracle.num_threads()
+        oracle.set_num_threads(n)
+        try:
+            return fn()
+        finally:
+            oracle.set_num_threads(old)
+
+    for spec, budget in ((W.C1, 1.0), (W.C2, 2.0)):
+        q, pool_h, compact = _decode_inputs_host(spec, dev)
+        call = lambda: oracle.sparse_mla(q, pool_h, compact, spec.sm_scale)
+        n, dt = _time_oracle(call, budget)
+        d = {"unit_of_work": "decode call: %d requests x %d heads x %d keys" % (spec.n_req, spec.n_heads, spec.k),
+             "ms_per_call": round(dt / n * 1e3, 3), "tokens_per_s": round(spec.n_req * n / dt, 2),
+             "threads": threads, "runs": n}
+        if spec is W.C1:
+            n1, dt1 = with_threads(1, lambda: _time_oracle(call, budget))
+            d["one_thread"] = {"ms_per_call": round(dt1 / n1 * 1e3, 3), "tokens_per_s": round(spec.n_req * n1 / dt1, 2),
+                               "runs": n1}
+        out[spec.name] = d
+
+    spec = W.C4
+    rows, wslots = W.write_tokens(spec), W.write_slots(spec)
+    pool_h = np.zeros((spec.n_slots, 352), dtype=np.uint8)
+    lists = W.dup_lists(spec)
+    write = lambda: oracle.quant_write(rows, wslots, pool_h)
+    dedup = lambda: oracle.dedup_compact(lists)
+    d = {"unit_of_work": "write of %d tokens; dedup of %d lists of %d" % (spec.n_tokens, spec.n_lists, spec.list_len),
+         "threads": threads}
+    for name, fn, budget in (("write", write, 1.5), ("dedup", dedup, 1.5)):
+        n, dt = _time_oracle(fn, budget)
+        n1, dt1 = with_threads(1, lambda: _time_oracle(fn, budget))
+        d[name] = {"us": round(dt / n * 1e6, 1), "runs": n, "one_thread_us": round(dt1 / n1 * 1e6, 1),
+                   "one_thread_runs": n1}
+    out[spec.name] = d
+
+    spec = W.C5
+    n_rows = 128
+    kv = W.kv_rows_host(spec, 0, spec.n_slots)
+    pool_h = np.zeros((spec.n_slots, 352), dtype=np.uint8)
+    oracle.quant_write(kv, np.arange(spec.n_slots, dtype=np.int32), pool_h)
+    del kv
+    sel = np.linspace(0, spec.rows - 1, n_rows).astype(np.int64)      # rows spread over all positions
+    import torch
+    q = W.queries(spec)[torch.from_numpy(sel)].float().numpy()
+    topk, pt, rr = W.topk_lists(spec)[sel], W.page_table(spec), W.row_req(spec)[sel]
+    n, dt = _time_oracle(lambda: oracle.sparse_mla(q, pool_h, topk, spec.sm_scale, page_table=pt, row_req=rr), 3.0)
+    per_row = dt / n / n_rows
+    out[spec.name] = {"unit_of_work": "prefill of %d of the %d query rows (evenly spaced) x %d heads x %d keys"
+                                      % (n_rows, spec.rows, spec.n_heads, spec.k),
+                      "ms_per_row": round(per_row * 1e3, 3), "runs": n, "threads": threads,
+                      "full_prefill_s_extrapolated": round(per_row * spec.rows, 2),
+                      "query_tokens_per_s": round(1.0 / per_row, 2)}
+    return out
 
 
 def main():
@@ -346,7 +446,7 @@ def main():
                    "q_dtype": spec.q_dtype, "splits": S, "rotating_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
-                     "kernel": "sparse_mla_kernel (per-split decode)", "avg_launch_ms": round(split_ms, 5),
+                     "kernel": "sparse_mla_bf16_kernel (per-split decode)", "avg_launch_ms": round(split_ms, 5),
                      "algorithmic_bytes": algo,
                      "mfma_tflops": round(decode_flops / (split_ms * 1e-3) / 1e12, 2),
                      "mfma_frac": round(decode_flops / (split_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
