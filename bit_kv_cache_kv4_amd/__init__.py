@@ -462,7 +462,8 @@ def global_compact(pool, topk, page_table=None, row_req=None, page_size=64, err_
 
 def gather_dequant(pool, topk, page_table=None, row_req=None, page_size=64, err_word=None, stream=None):
     """kv4_gather_dequant; returns (rows [R, k, D] float16, slots [R, k] int32), D = 576, or 512
-    for a rope-free (288-byte) pool."""
+    for a rope-free (288-byte) pool.  Within each chunk of 2048 entries the valid ones come first, in
+    list order (as the attention kernels hold them); the rest are zero rows with slot -1."""
     R, k = topk.shape[0], topk.shape[1]
     dim = LATENT if pool.dim() == 2 and pool.shape[1] == ROW_BYTES_ROPE_FREE else DIM
     a = _attn_args(_unread_q(pool, topk), pool, topk, 1.0, page_table, row_req, page_size, None, None, err_word)

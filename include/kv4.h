@@ -319,14 +319,18 @@ kv4_status kv4_merge_states_f16(const void *part_o, const float *part_lse, int32
                                 float *lse, void *stream);
 
 /*
- * Dequantizing gather (README, "4-bit KV cache": the dequantizing gather).
- * For query row r and list entry j < k (translated exactly as above), writes
- * the entry's D dequantized values (D = 576, or 512 for rope-free rows) as
- * fp16 bit patterns to out[(r * k + j) * D + i] and its pool slot to
- * slots_out[r * k + j]; skipped entries get D zeros and slot -1.  Every value
+ * Dequantizing gather (README, "4-bit KV cache": the dequantizing gather),
+ * through the attention kernels' own front end: each chunk of 2048 list
+ * entries of query row r (entries c0 .. c0 + 2047) is translated as above and
+ * its valid entries are packed to the chunk's front in list order, exactly as
+ * the attention kernels hold them in their K tiles.  Output position
+ * r * k + c0 + i receives the chunk's i-th valid entry: its D dequantized
+ * values (D = 576, or 512 for rope-free rows) as fp16 bit patterns at
+ * out[(r * k + c0 + i) * D + d] and its pool slot at slots_out[r * k + c0 + i];
+ * positions past the chunk's valid count get D zeros and slot -1.  Every value
  * is exact in fp16 (an E2M1 x E4M3 product or an E4M3 value).  The attention
- * entry points never build this copy; it serves callers that want the rows
- * themselves.
+ * entry points never build this copy; it serves tests and callers that want
+ * the rows themselves.
  *   out           device [n_rows, k, D] uint16 (fp16 bits), 16-byte aligned.
  *   slots_out     device [n_rows, k] int32, nullable.
  * a->q, a->q_dtype, its strides, a->n_heads, a->out and a->lse are ignored (q
