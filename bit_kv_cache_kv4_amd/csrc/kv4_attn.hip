@@ -53,6 +53,7 @@
 #include "kv4_attn.h"
 #include "kv4_device.h"
 
+#include <algorithm>
 #include <type_traits>
 
 
@@ -1455,91 +1456,114 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 
 // ----------------------------------------------------------------- merge
 
-// One 128-thread workgroup per state t; a thread owns 4 dims per 512.  With
-// at most kMergeBatch parts of at most 512 dims (decode's case), the parts' o
-// are loaded before the weights are formed, so their round trip overlaps that
-// of the lse.  With M the largest lse: w_s = exp(lse_s - M) (an empty part
-// weighs 0), W = the w_s summed in part order, o = (the w_s o_s summed in part
-// order) / W, lse = M + ln W; all parts empty gives o = 0, lse = -inf.
-constexpr int kMergeBatch = 8;
+// One wavefront per state t and 256 dims of it; a lane owns 4 consecutive
+// dims.  Lane s loads part s's lse (at most 64 parts) and computes its weight;
+// the lanes read the maximum, the weights and their sum across the wavefront,
+// so there is no LDS and no barrier.  With at most 32 parts (decode's case) the
+// parts' o are loaded together with the lse, one round trip for all.  With M the
+// largest lse: w_s = exp(lse_s - M) (an empty part weighs 0), W = the w_s
+// summed in part order, o = (the w_s o_s summed in part order) / W, lse = M +
+// ln W; all parts empty gives o = 0, lse = -inf.
+constexpr int kMergeSeg = 256;                 // dims per wavefront
+constexpr int kMergeWaves = 4;                 // wavefronts per workgroup
 
-// four consecutive dims of one part's o, widened to fp32 (exact) from fp16 parts
+// four consecutive dims of one part's o as stored (fp16 parts stay fp16 until
+// used), and widened to fp32 (exact)
 template <bool F16>
-__device__ __forceinline__ floatx4_t load_part4(const MergeParams &p, int64_t off) {
-    if constexpr (F16) return __builtin_convertvector(*reinterpret_cast<const half4_t *>(p.part_o_h + off), floatx4_t);
+using PartPiece = std::conditional_t<F16, half4_t, floatx4_t>;
+template <bool F16>
+__device__ __forceinline__ PartPiece<F16> load_piece(const MergeParams &p, int64_t off) {
+    if constexpr (F16) return *reinterpret_cast<const half4_t *>(p.part_o_h + off);
     else return *reinterpret_cast<const floatx4_t *>(p.part_o + off);
+}
+template <bool F16>
+__device__ __forceinline__ floatx4_t widen(PartPiece<F16> x) {
+    if constexpr (F16) return __builtin_convertvector(x, floatx4_t);
+    else return x;
+}
+
+// task = (state t, segment of 256 dims) for the calling wavefront.  B > 0:
+// at most B parts, all loaded before any is used (a part past the last
+// re-reads the last; it is not used); B = 0: any count, loaded as used.
+template <bool F16, int B>
+__device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, int n_seg, int lane) {
+    const int64_t t = task / n_seg;
+    const int seg = (int)(task - t * n_seg);
+    const int d = seg * kMergeSeg + 4 * lane;
+    const bool live = d < p.dim;
+    const int S = p.n_parts;
+    const int64_t o_t = t * p.dim + (live ? d : 0);            // part s at s * n_states * dim
+    const int64_t o_stride = p.n_states * (int64_t)p.dim;
+    // lane s holds part s's lse and, once M is known, its weight; every lane
+    // reads them from there in part order
+    // (no load sits under a branch, so none waits for another)
+    const float my_raw = p.part_lse[t + (int64_t)min(lane, S - 1) * p.n_states];
+    PartPiece<F16> v[B > 0 ? B : 1];
+    if constexpr (B > 0) {
+#pragma unroll
+        for (int s = 0; s < B; ++s) v[s] = load_piece<F16>(p, o_t + min(s, S - 1) * o_stride);
+    }
+    const float my = lane < S ? my_raw : -__builtin_inff();
+    auto lane_val = [](float x, int s) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), s));
+    };
+    float M = -__builtin_inff();
+    for (int s = 0; s < S; ++s) M = __builtin_fmaxf(M, lane_val(my, s));
+    const float my_w = my == -__builtin_inff() || M == -__builtin_inff() ? 0.0f : expf(my - M);
+    auto weight = [&](int s) { return lane_val(my_w, s); };
+    float W = 0.0f;
+    if (M != -__builtin_inff())
+        for (int s = 0; s < S; ++s) W += weight(s);
+    if (seg == 0 && lane == 0 && p.lse) p.lse[t] = M == -__builtin_inff() ? M : M + logf(W);
+    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+    floatx4_t acc = {0, 0, 0, 0};
+    if (W > 0.0f) {
+        if constexpr (B > 0) {
+#pragma unroll
+            for (int s = 0; s < B; ++s) {
+                if (s < S) {
+                    const float ws = weight(s);
+                    if (ws != 0.0f) acc += ws * widen<F16>(v[s]);
+                }
+            }
+        } else {
+            for (int s = 0; s < S; ++s) {
+                const float ws = weight(s);
+                if (ws != 0.0f) acc += ws * widen<F16>(load_piece<F16>(p, o_t + s * o_stride));
+            }
+        }
+    }
+    float *orow = p.out + (t / p.states_per_row) * p.out_row_stride + (t % p.states_per_row) * p.out_col_stride;
+    if (live) *reinterpret_cast<floatx4_t *>(orow + d) = acc * inv;
+}
+
+// wavefronts take tasks in order, the grid's wavefronts apart
+template <bool F16, int B>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_states_kernel(MergeParams p) {
+    const int n_seg = (p.dim + kMergeSeg - 1) / kMergeSeg;
+    const int64_t tasks = p.n_states * n_seg;
+    const int64_t stride = (int64_t)gridDim.x * kMergeWaves;
+    for (int64_t task = (int64_t)blockIdx.x * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         task < tasks; task += stride)
+        merge_task<F16, B>(p, task, n_seg, threadIdx.x & 63);
 }
 
 template <bool F16>
-__global__ __launch_bounds__(128) void merge_states_kernel(MergeParams p) {
-    __shared__ float w[64];
-    __shared__ float stat[2];
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int S = p.n_parts;
-    const int64_t o_t = t * p.dim;                                // part s at s * n_states * dim
-    const int64_t o_stride = p.n_states * (int64_t)p.dim;
-    const bool early = S <= kMergeBatch && p.dim <= 512;          // uniform
-    floatx4_t v[kMergeBatch];
-    if (early && 4 * tid < p.dim) {
-#pragma unroll
-        for (int s = 0; s < kMergeBatch; ++s)
-            if (s < S) v[s] = load_part4<F16>(p, o_t + s * o_stride + 4 * tid);
-    }
-    if (tid == 0) {
-        float M = -__builtin_inff();
-        for (int s = 0; s < S; ++s) M = __builtin_fmaxf(M, p.part_lse[(int64_t)s * p.n_states + t]);
-        stat[0] = M;
-    }
-    __syncthreads();
-    const float M = stat[0];
-    if (M != -__builtin_inff() && tid < S) {
-        const float ls = p.part_lse[(int64_t)tid * p.n_states + t];
-        w[tid] = ls == -__builtin_inff() ? 0.0f : expf(ls - M);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float W = 0.0f;
-        if (M != -__builtin_inff())
-            for (int s = 0; s < S; ++s) W += w[s];
-        stat[1] = W;
-        if (p.lse) p.lse[t] = M == -__builtin_inff() ? M : M + logf(W);
-    }
-    __syncthreads();
-    const float W = stat[1];
-    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-    float *orow = p.out + (t / p.states_per_row) * p.out_row_stride + (t % p.states_per_row) * p.out_col_stride;
-    if (early) {
-        if (4 * tid < p.dim) {
-            floatx4_t acc = {0, 0, 0, 0};
-            if (W > 0.0f) {
-#pragma unroll
-                for (int s = 0; s < kMergeBatch; ++s) {
-                    if (s < S) {
-                        const float ws = w[s];
-                        if (ws != 0.0f) acc += ws * v[s];
-                    }
-                }
-            }
-            *reinterpret_cast<floatx4_t *>(orow + 4 * tid) = acc * inv;
-        }
-        return;
-    }
-    for (int d = 4 * tid; d < p.dim; d += 512) {
-        floatx4_t acc = {0, 0, 0, 0};
-        if (W > 0.0f)
-            for (int s = 0; s < S; ++s) {
-                const float ws = w[s];
-                if (ws != 0.0f) acc += ws * load_part4<F16>(p, o_t + s * o_stride + d);
-            }
-        *reinterpret_cast<floatx4_t *>(orow + d) = acc * inv;
-    }
+void launch_merge(const MergeParams &p, dim3 grid, dim3 block, hipStream_t stream) {
+    if (p.n_parts <= 4) hipLaunchKernelGGL((merge_states_kernel<F16, 4>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 8) hipLaunchKernelGGL((merge_states_kernel<F16, 8>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 16) hipLaunchKernelGGL((merge_states_kernel<F16, 16>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 32) hipLaunchKernelGGL((merge_states_kernel<F16, 32>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_states_kernel<F16, 0>), grid, block, 0, stream, p);
 }
 
 hipError_t launch_merge_states(const MergeParams &p, hipStream_t stream) {
     if (p.n_states == 0) return hipSuccess;
-    if (p.part_o_h) hipLaunchKernelGGL(merge_states_kernel<true>, dim3((unsigned)p.n_states), dim3(128), 0, stream, p);
-    else hipLaunchKernelGGL(merge_states_kernel<false>, dim3((unsigned)p.n_states), dim3(128), 0, stream, p);
+    const int64_t tasks = p.n_states * ((p.dim + kMergeSeg - 1) / kMergeSeg);
+    const dim3 grid((unsigned)std::min<int64_t>((tasks + kMergeWaves - 1) / kMergeWaves, 1 << 20)),
+        block(64 * kMergeWaves);
+    if (p.part_o_h) launch_merge<true>(p, grid, block, stream);
+    else launch_merge<false>(p, grid, block, stream);
     return hipGetLastError();
 }
 

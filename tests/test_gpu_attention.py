@@ -230,6 +230,24 @@ def test_other_page_sizes(page_size):
     _run(spec, W.queries(spec), W.topk_lists(spec), pt, page_size=page_size)
 
 
+@pytest.mark.parametrize("n_pages", [4096, 4097, 9000])
+def test_long_page_table_rows(n_pages):
+    """Page-table rows of 4096 to 9000 entries over 16-token pages, naming
+    physical pages more than once; the last position of the table and one past
+    it; decode with bf16 and fp32 queries, and prefill."""
+    spec = W.scaled(SMALL, n_req=2, ctx=16 * n_pages, k=300)
+    g = np.random.default_rng(n_pages)
+    pt = g.integers(0, spec.n_slots // 16, size=(spec.n_req, n_pages)).astype(np.int32)
+    q, topk = W.queries(spec), W.topk_lists(spec).copy()
+    topk[0, 0] = spec.ctx - 1
+    _run(spec, q, topk, pt, page_size=16)
+    _run(spec, q, topk, pt, page_size=16, num_splits=2)
+    _run(W.scaled(spec, q_dtype="f32"), W.queries(W.scaled(spec, q_dtype="f32")), topk, pt, page_size=16)
+    _run(spec, q, topk, pt, page_size=16, prefill=True, row_req=np.int32([1, 0]))
+    topk[1, 3] = spec.ctx
+    _run(spec, q, topk, pt, page_size=16, err_expect=kv4.ERRBIT_PAGE)
+
+
 # ------------------------------------------------- the path is exercised
 def test_unselected_rows_do_not_matter_selected_rows_do():
     spec = SMALL

@@ -113,6 +113,21 @@ def test_gather_lists_longer_than_a_chunk():
     _check(spec, topk, W.page_table(spec), pools=pools)
 
 
+@pytest.mark.parametrize("n_pages", [4096, 4097])
+def test_gather_long_page_table_rows(n_pages):
+    """Page-table rows of 4096 and 4097 entries naming pool pages more than
+    once; entries in both chunks of a 2100-entry list."""
+    spec = W.scaled(W.C2, n_req=2, ctx=64 * n_pages, n_pool_pages=160, k=2100, seed=2300)
+    pools = build_pools(spec)
+    g = np.random.default_rng(n_pages)
+    pt = g.integers(0, spec.n_pool_pages, size=(spec.n_req, n_pages)).astype(np.int32)
+    topk = W.topk_lists(spec).copy()
+    topk[0, 0] = spec.ctx - 1
+    _check(spec, topk, pt, pools=pools)
+    topk[1, 2049] = spec.ctx                         # past the table, in the second chunk
+    _check(spec, topk, pt, err_expect=kv4.ERRBIT_PAGE, pools=pools)
+
+
 def _code_pool(n_rope):
     """Eight rows holding every (E2M1 code, E4M3 scale byte) pair once: block b
     of row i has scale byte 32 i + b (all 256, NaN bytes and negative scales

@@ -52,8 +52,8 @@ def _compare(out, lse, o_ref, lse_ref):
     return float(rel.max())
 
 
-@pytest.mark.parametrize("n_parts", [1, 2, 8, 9, 33, 64])
-@pytest.mark.parametrize("dim", [4, 64, 512, 576, 4096])
+@pytest.mark.parametrize("n_parts", [1, 2, 8, 9, 16, 17, 33, 64])
+@pytest.mark.parametrize("dim", [4, 64, 260, 512, 576, 4096])
 def test_merge_matches_oracle(n_parts, dim):
     n_states = 37 if dim >= 4096 else 301
     o, lse = _parts(n_parts, n_states, dim, seed=7000 + 131 * n_parts + dim)
@@ -81,3 +81,14 @@ def test_merge_into_strided_output_rows():
     torch.cuda.synchronize()
     _compare(out, l, o_ref, lse_ref)
     assert (wide[:, dim:] == 7.0).all(), "the merge wrote outside its rows"
+
+
+def test_merge_millions_of_states():
+    """4.3M states of 4 dims: more wavefront tasks than one launch has
+    wavefronts, so wavefronts take several states each."""
+    n_parts, n_states, dim = 2, 4_300_000, 4
+    o, lse = _parts(n_parts, n_states, dim, seed=7200)
+    o_ref, lse_ref = oracle.merge_states(o.astype(np.float64), lse.astype(np.float64))
+    out, l = kv4.merge_states(torch.from_numpy(o).to(DEV), torch.from_numpy(lse).to(DEV))
+    torch.cuda.synchronize()
+    _compare(out, l, o_ref, lse_ref)
