@@ -97,6 +97,7 @@ constexpr float kRefSlack = 15.0f;                     // log2 headroom of fp16 
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 // K-tile layout: element (row r, chunk c of 8 dims) at c * 512 + 16 * (r ^ 4 (c & 3)),
 // i.e. the 32 rows' copies of a 16-byte chunk are contiguous, their order
@@ -916,13 +917,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     uint32_t err = 0;
 
     // ---- Prologue.  Three dependent round trips (list entries, page-table
-    // entries, the first rows) come before the first tile, so nothing queues
-    // ahead of them: the list, the page-table entries once it is back, then
-    // this row's queries (74 KB: consecutive threads take consecutive 16-byte
-    // chunks of a head's row), the slots packed, each role's first gathers,
-    // and only then the queries staged in LDS, in the third K tile and the P
-    // buffers (untouched until the first tile's softmax; rows padded by 16
-    // bytes).
+    // entries, the first rows) come before the first tile.  The list goes
+    // out first, then this row's queries (74 KB: consecutive threads take
+    // consecutive 16-byte chunks of a head's row), then the page-table entries
+    // once the list is back; while those are in flight the queries are
+    // converted to fp16 and staged in LDS (in the third K tile and the P
+    // buffers, untouched until the first tile's softmax; rows padded by 16
+    // bytes), and the slot packing's barrier orders them before their
+    // readers.
     constexpr int kQRow = kD * 2 + 16;
     constexpr int kQChunks = kD * 2 / 16;
     constexpr int kTPH = kThreads / 64;                    // threads per head row
@@ -936,25 +938,57 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
 
     int32_t pos[kPosPerLane], phys[kPosPerLane];
     const int first_hi = min(e_hi, e_lo + kSlotCap);
-    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
-    load_pages(p, lc, pos, phys);
-    {
-        const int head = h0 + q_hh;
-        const uint8_t *src = qr + (int64_t)min(head, p.n_heads - 1) * p.q_head_stride * 2 + 16 * q_part;
+    // The queries as the score MFMAs take them, made by every thread from the
+    // 72 values it loaded: a head's 8 threads (consecutive lanes) agree on its
+    // largest |q| (non-negative bf16 values order as integers; NaN counts as
+    // infinity), whose power-of-two scale qs puts it in [2^13, 2^14), exact
+    // in fp16; each value becomes fp16(q qs) (exact unless below fp16's
+    // normal range) in place of its bf16, and the head's qs goes to q_scale.
+    // Heads past the last take zeros.
+    float *q_scale = red;                          // [head]; red is next written after the first tile
+    auto stage_q = [&]() {
+        const uint32_t keep = h0 + q_hh < p.n_heads ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) qc[i] &= keep;
+        ushort2_t m2 = {0, 0};
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(ushort2_t, qc[i][c] & 0x7FFF7FFFu));
+        uint32_t mb = min(max((uint32_t)m2[0], (uint32_t)m2[1]), 0x7F80u);
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 1));
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 2));
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 4));
+        const float qmax = __uint_as_float(mb << 16);
+        int ex = 0;
+        if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
+        const float qs = __builtin_ldexpf(1.0f, 14 - ex);
+        if (q_part == 0) q_scale[q_hh] = qs;
+        const uint32_t dst = Lq + q_hh * kQRow + 16 * q_part;
 #pragma unroll
         for (int i = 0; i < kQPer; ++i) {
-            qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
-            if (head >= p.n_heads) qc[i] = u32x4_t{0, 0, 0, 0};
+            half8_t h;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                h[2 * c] = (_Float16)(__uint_as_float(qc[i][c] << 16) * qs);
+                h[2 * c + 1] = (_Float16)(__uint_as_float(qc[i][c] & 0xFFFF0000u) * qs);
+            }
+            lds_st<half8_t>(dst + 16 * kTPH * i, h);
         }
+    };
+
+    load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
+    {
+        const uint8_t *src = qr + (int64_t)min(h0 + q_hh, p.n_heads - 1) * p.q_head_stride * 2 + 16 * q_part;
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
     }
+    load_pages(p, lc, pos, phys);
+    stage_q();
     int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
     if (tid == 0) *flag = 0;
     __syncthreads();
-    auto stage_q = [&]() {
-        const uint32_t dst = Lq + q_hh * kQRow + 16 * q_part;
-#pragma unroll
-        for (int i = 0; i < kQPer; ++i) lds_st<u32x4_t>(dst + 16 * kTPH * i, qc[i]);
-    };
 
     const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
     int n_t = 0, n_real = 0, last_rows = kTile;
@@ -1009,8 +1043,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
             gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
             gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
         }
-        stage_q();
-        __syncthreads();                           // every head row staged
 
         // k-step ks of lane group q4 covers chunk C(ks, q4) = 8 (ks / 2) +
         // 2 (ks % 2) + cq, cq = q4 / 2 + 4 (q4 % 2): the two 16-lane groups of
@@ -1021,39 +1053,16 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         // scores as long as queries and keys share it.
         const int cq = (q4 >> 1) + 4 * (q4 & 1);
         // queries: B operand of S^T = K Q^T.  Lane (l16, q4) holds head h0 +
-        // 32 hg + 16 hb + l16, dims 8 C(ks, q4) .. +7.  The power-of-two scale
-        // qs puts the head's largest |q| in [2^13, 2^14), exact in fp16;
+        // 32 hg + 16 hb + l16, dims 8 C(ks, q4) .. +7, as staged in fp16;
         // score_mul = sm_scale log2(e) / qs turns scores into log2 units.
         half8_t qb[2][kKs];
         float score_mul[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
             const uint32_t qf = Lq + (32 * hg + 16 * hb + l16) * kQRow + 16 * cq;
-            float qmax = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) {     // read twice (maximum, conversion): fewer live registers
-                const u32x4_t v = lds_ld<u32x4_t>(qf + 128 * (ks >> 1) + 32 * (ks & 1));
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fabsf(__uint_as_float(v[c] << 16)),
-                                                                 __builtin_fabsf(__uint_as_float(v[c] & 0xFFFF0000u))));
-            }
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 16));
-            qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));
-            int ex = 0;
-            if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
-            const float qs = __builtin_ldexpf(1.0f, 14 - ex);
-            score_mul[hb] = p.score_mul / qs;
-            asm volatile("" ::: "memory");         // read again: the first pass's values are not kept
-#pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) {
-                const u32x4_t v = lds_ld<u32x4_t>(qf + 128 * (ks >> 1) + 32 * (ks & 1));
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    qb[hb][ks][2 * c] = (_Float16)(__uint_as_float(v[c] << 16) * qs);
-                    qb[hb][ks][2 * c + 1] = (_Float16)(__uint_as_float(v[c] & 0xFFFF0000u) * qs);
-                }
-            }
+            for (int ks = 0; ks < kKs; ++ks) qb[hb][ks] = lds_ld<half8_t>(qf + 128 * (ks >> 1) + 32 * (ks & 1));
+            score_mul[hb] = p.score_mul / q_scale[32 * hg + 16 * hb + l16];
         }
 
         // score operand (A of 16x16x32): row 16 rh + l16, chunk C(ks, q4), at
@@ -1251,8 +1260,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
             gather_units(0, G0);
             gather_units(1, G1);
         }
-        stage_q();
-        __syncthreads();                           // every head row staged
 
         // transposing reads (A of O^T = V^T P^T), as in the fp32-query kernel
         const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), j4 = (lane >> 2) & 3;
