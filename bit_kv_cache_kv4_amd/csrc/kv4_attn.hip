@@ -1075,9 +1075,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         const int row0 = 16 * rh + 4 * q4;         // this lane's first row
 
         float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
-        float m_max[2] = {-__builtin_inff(), -__builtin_inff()};
+        float m_rel[2] = {-__builtin_inff(), -__builtin_inff()};   // largest s - m_ref of this pass
         float l_run[2] = {0.0f, 0.0f};
-        bool need_redo = false;
 
         auto scores = [&](uint32_t kb, floatx4_t (&acc)[2]) {
             const uint32_t a0 = kb + a_off0, a1 = kb + a_off1;
@@ -1127,22 +1126,26 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         };
         // P = 2^(s - m_ref) of this lane's 4 rows x 2 heads into P buffer pb;
         // rows >= lim are padding
+        // (the padding rows' masking only in a chunk's last tile, a uniform
+        // branch; whether P could overflow fp16 is judged from m_rel once per
+        // pass)
         auto softmax = [&](const floatx4_t (&acc)[2], int lim, int pb) {
             float e[2][4];
-            float emax = -__builtin_inff();
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                float hm = -__builtin_inff();
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e[hb][i] = __builtin_fmaf(acc[hb][i], score_mul[hb], -m_ref[hb]);
-                    if (lim < kTile && row0 + i >= lim) e[hb][i] = -__builtin_inff();
-                    hm = __builtin_fmaxf(hm, e[hb][i]);
-                }
-                m_max[hb] = __builtin_fmaxf(m_max[hb], hm + m_ref[hb]);
-                emax = __builtin_fmaxf(emax, hm);
+                for (int i = 0; i < 4; ++i) e[hb][i] = __builtin_fmaf(acc[hb][i], score_mul[hb], -m_ref[hb]);
+            if (lim < kTile) {
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (row0 + i >= lim) e[hb][i] = -__builtin_inff();
             }
-            need_redo |= emax > kRefSlack;         // P could overflow fp16
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+                m_rel[hb] = __builtin_fmaxf(m_rel[hb], __builtin_fmaxf(__builtin_fmaxf(e[hb][0], e[hb][1]),
+                                                                        __builtin_fmaxf(e[hb][2], e[hb][3])));
             const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
@@ -1173,6 +1176,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         };
 
         for (int pass = 0; pass < 2; ++pass) {
+            m_rel[0] = m_rel[1] = -__builtin_inff();
             l_run[0] = l_run[1] = 0.0f;
             for (int c_lo = e_lo; c_lo < e_hi; c_lo += kSlotCap) {
                 const int c_hi = min(e_hi, c_lo + kSlotCap);
@@ -1222,7 +1226,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                     bB = a0;
                 }
             }
-            if (need_redo) *flag = 1;
+            if (__builtin_fmaxf(m_rel[0], m_rel[1]) > kRefSlack) *flag = 1;   // P could have overflowed fp16
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {       // this pass's row sums and reference
                 float l2 = l_run[hb] + __shfl_xor(l_run[hb], 16);
@@ -1235,7 +1239,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
             // second pass: the exact maximum of every head as its reference
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
-                float mm = __builtin_fmaxf(m_max[hb], __shfl_xor(m_max[hb], 16));
+                // the largest e + m_ref of the pass: rounding is monotonic, so
+                // adding m_ref after the maximum gives the same value
+                const float m_abs = m_rel[hb] + m_ref[hb];
+                float mm = __builtin_fmaxf(m_abs, __shfl_xor(m_abs, 16));
                 mm = __builtin_fmaxf(mm, __shfl_xor(mm, 32));
                 if (q4 == 0) red[(hg * 2 + rh) * 32 + 16 * hb + l16] = mm;
             }
