@@ -1275,7 +1275,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         const uint32_t px_r = L + kOffP2 + l32 * kPXHead + 2 * (8 * g);
         floatx16_t o[4][2];
 
-        auto pv = [&](uint32_t kb, int pb, uint32_t kd, GSet<ROPE> &G, int next_tile) {
+        auto pv = [&](uint32_t kb, int pb, uint32_t kd, GSet<ROPE> &G, int32_t next) {
             const uint32_t t0 = kb + tr_off0, t1 = kb + tr_off1;
             half8_t pbv[2][2];
 #pragma unroll
@@ -1303,7 +1303,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 if constexpr (j + kTrAhead < 8) issue(j + kTrAhead);
                 if constexpr (j == 0) dd = dq_scales<ROPE>(G, gp);
                 if constexpr (j >= 1 && j <= 4) dq_chunk<ROPE>(kd, gr, gp, j - 1, dd, G);   // between the MFMAs
-                if constexpr (j == 5) gather_units(next_tile, G);                         // G consumed: refill
+                if constexpr (j == 5) gather_set<ROPE, false>(p.pool, stand_in, next, gp, G);   // G consumed: refill
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
@@ -1311,7 +1311,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         // 256..511; it runs whether t + 2 exists or not, as on the score
         // side) and then the gather of t + 4 between its MFMAs
         auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bA, uint32_t bC) {
-            pv(bA, t & 1, bC, G, min(t + 4, n_t - 1));
+            // the slot read first: waiting for it later would wait for every
+            // LDS access issued since
+            const int32_t next = slots[min(t + 4, n_t - 1) * kTile + gr];
+            pv(bA, t & 1, bC, G, next);
             __syncthreads();
         };
 
