@@ -1292,7 +1292,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
 #pragma unroll
             for (int j = 0; j < kTrAhead; ++j) issue(j);
             __builtin_amdgcn_sched_barrier(0);
-            half2_t dd;
             static_for<0, 8>([&](auto step) {
                 constexpr int j = decltype(step)::value;
                 constexpr int md = j & 3, kk = j >> 2;
@@ -1301,15 +1300,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 o[md][0] = mfma32(a, pbv[0][kk], o[md][0]);
                 o[md][1] = mfma32(a, pbv[1][kk], o[md][1]);
                 if constexpr (j + kTrAhead < 8) issue(j + kTrAhead);
-                if constexpr (j == 0) dd = dq_scales<ROPE>(G, gp);
-                if constexpr (j >= 1 && j <= 4) dq_chunk<ROPE>(kd, gr, gp, j - 1, dd, G);   // between the MFMAs
-                if constexpr (j == 5) gather_set<ROPE, false>(p.pool, stand_in, next, gp, G);   // G consumed: refill
                 __builtin_amdgcn_sched_barrier(0);
             });
+            // the dequantization after the MFMAs are issued: the matrix pipe
+            // is then this wavefront's alone (the score wavefront's MFMAs are
+            // done), so the conversions overlap its last MFMAs
+            const half2_t dd = dq_scales<ROPE>(G, gp);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dq_chunk<ROPE>(kd, gr, gp, i, dd, G);
+            gather_set<ROPE, false>(p.pool, stand_in, next, gp, G);   // G consumed: refill
         };
-        // phase: P.V of t with the dequantization of t + 2 (latent dims
+        // phase: P.V of t, then the dequantization of t + 2 (latent dims
         // 256..511; it runs whether t + 2 exists or not, as on the score
-        // side) and then the gather of t + 4 between its MFMAs
+        // side) and the gather of t + 4
         auto iteration = [&](int t, GSet<ROPE> &G, uint32_t bA, uint32_t bC) {
             // the slot read first: waiting for it later would wait for every
             // LDS access issued since
