@@ -329,14 +329,13 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_f32q_kernel(AttnParams p)
     uint32_t err = 0;
 
     // ---- Prologue.  Three dependent round trips (list entries, page-table
-    // entries, the first rows) come before the first tile, so nothing may queue
-    // ahead of them: the list, then the page-table entries once it is back,
-    // then this row's queries (coalesced: consecutive threads take consecutive
-    // 16-byte chunks of a head's row; 74 KB, whose loads would otherwise hold
-    // up the page-table loads), the slots packed, the first gathers issued,
-    // and only then the queries staged in LDS (rows padded so the fragment
-    // reads are conflict-free).
-    // All 64 fp32 head rows are staged at once; they fill most of the LDS
+    // entries, the first rows) come before the first tile.  The list goes out
+    // first, then this row's queries (coalesced: consecutive threads take
+    // consecutive 16-byte chunks of a head's row; 147 KB), then the page-table
+    // entries once the list is back; while those are in flight the queries are
+    // converted and staged in LDS (rows padded so the fragment reads are
+    // conflict-free), and the slot packing's barrier orders them before their
+    // readers.  All 64 head rows are staged at once; they fill most of the LDS
     // (the slot list lies beyond), and a barrier separates their last read
     // from the first K-tile store.
     constexpr int kQE = 4;                                 // bytes per query element
@@ -354,19 +353,70 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_f32q_kernel(AttnParams p)
     static_assert(kQChunks == kTPH * kQPer, "query chunks do not divide");
     const uint8_t *qr = reinterpret_cast<const uint8_t *>(p.q) + (int64_t)r * p.q_row_stride * kQE;
     const int q_hh = tid / kTPH, q_part = tid % kTPH;
-    auto load_q = [&](u32x4_t (&qc)[kQPer]) {
-        const int head = h0 + q_hh;
-        const uint8_t *src = qr + (int64_t)min(head, p.n_heads - 1) * p.q_head_stride * kQE + 16 * q_part;
+    auto load_q = [&](u32x4_t (&qc)[kQPer]) {   // heads past the last re-read the last one (zeroed when staged)
+        const uint8_t *src = qr + (int64_t)min(h0 + q_hh, p.n_heads - 1) * p.q_head_stride * kQE + 16 * q_part;
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
+    };
+    // The queries as the score MFMAs take them, made by every thread from the
+    // 72 values it loaded (chunk q_part + 8 i holds dims 4 (q_part + 8 i) ..
+    // +3; chunks i < kHalfI lie in the first half of the dims): per head and
+    // half, the head's 8 threads (consecutive lanes) agree on the largest |q|,
+    // whose power-of-two scale qs puts it in [2^13, 2^14); each q qs becomes a
+    // hi and a lo fp16 part, hi at byte 2d of the head's staging row and lo at
+    // 2 kD + 2d, and qs goes to q_scale[2 head + half].  Wavefronts whose heads
+    // are all past the last only store zeros.
+    constexpr int kHalfI = kHd / (4 * kTPH);
+    static_assert(kHd % (4 * kTPH) == 0, "a thread's chunks do not split at the half");
+    float *q_scale = red;                          // [head][half]; red is next written after the first tile
+    auto stage_q = [&](const u32x4_t (&qc)[kQPer]) {
+        const uint32_t dst = Lq + q_hh * kQRow + 8 * q_part;
+        if (__builtin_amdgcn_readfirstlane(h0 + 8 * w) >= p.n_heads) {   // the wavefront's 8 heads are all dead
+#pragma unroll
+            for (int i = 0; i < kQPer; ++i) {
+                lds_st<u32x2_t>(dst + 8 * kTPH * i, u32x2_t{0, 0});
+                lds_st<u32x2_t>(dst + 2 * kD + 8 * kTPH * i, u32x2_t{0, 0});
+            }
+            if (q_part == 0) q_scale[2 * q_hh] = q_scale[2 * q_hh + 1] = 1.0f;
+            return;
+        }
+        const bool live = h0 + q_hh < p.n_heads;
+        float m[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < kQPer; ++i) {
-            qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
-            if (head >= p.n_heads) qc[i] = u32x4_t{0, 0, 0, 0};
+            const floatx4_t v = __builtin_bit_cast(floatx4_t, qc[i]);
+            m[i >= kHalfI] = __builtin_fmaxf(m[i >= kHalfI],
+                                             __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                                             __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
         }
-    };
-    auto stage_q = [&](const u32x4_t (&qc)[kQPer]) {
-        const uint32_t dst = Lq + q_hh * kQRow + 16 * q_part;
+        float qs[2];
 #pragma unroll
-        for (int i = 0; i < kQPer; ++i) lds_st<u32x4_t>(dst + 16 * kTPH * i, qc[i]);
+        for (int h = 0; h < 2; ++h) {
+            float mm = live ? m[h] : 0.0f;
+            mm = __builtin_fmaxf(mm, __shfl_xor(mm, 1));
+            mm = __builtin_fmaxf(mm, __shfl_xor(mm, 2));
+            mm = __builtin_fmaxf(mm, __shfl_xor(mm, 4));
+            int ex = 0;
+            if (mm > 0.0f) (void)__builtin_frexpf(mm, &ex);
+            qs[h] = __builtin_ldexpf(1.0f, 14 - ex);     // the largest |q| times qs < 2^14
+        }
+        if (q_part == 0) {
+            q_scale[2 * q_hh] = qs[0];
+            q_scale[2 * q_hh + 1] = qs[1];
+        }
+#pragma unroll
+        for (int i = 0; i < kQPer; ++i) {
+            const floatx4_t v = __builtin_bit_cast(floatx4_t, qc[i]);
+            half4_t hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = live ? v[e] * qs[i >= kHalfI] : 0.0f;
+                hi[e] = (_Float16)x;
+                lo[e] = (_Float16)(x - (float)hi[e]);
+            }
+            lds_st<half4_t>(dst + 8 * kTPH * i, hi);
+            lds_st<half4_t>(dst + 2 * kD + 8 * kTPH * i, lo);
+        }
     };
 
     int32_t pos[kPosPerLane], phys[kPosPerLane];
@@ -438,50 +488,22 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_f32q_kernel(AttnParams p)
         // wavefronts gather and dequantize whole rows)
 
         // queries: B operand of S^T = K Q^T.  Lane (l32, g) holds head h0 +
-        // 32hg + l32, dims kHd half + 16 ks + 8 g .. +7 for ks < kKs.  The
-        // power-of-two scale qs puts the largest |q| of the head's half in
-        // [2^13, 2^14); each fp32 query becomes a hi and a lo fp16 part (two
-        // MFMAs per k-step).  Each half has its own scale: its partial scores
-        // are multiplied by score_mul = sm_scale log2(e) / qs before the two
-        // halves are added, so no exchange between them is needed here.
+        // 32hg + l32, dims kHd half + 16 ks + 8 g .. +7 for ks < kKs, as
+        // staged: a hi and a lo fp16 part (two MFMAs per k-step) at the scale
+        // of the head's half.  Each half's partial scores are multiplied by
+        // score_mul = sm_scale log2(e) / qs before the two halves are added,
+        // so no exchange between them is needed here.
         half8_t qb[kKs];
         half8_t ql[kKs];
-        float score_mul = 0.0f;
+        float score_mul;
         {
-            const uint32_t qf = Lq + (32 * hg + l32) * kQRow + kQE * (kHd * half + 8 * g);
-            auto scale_of = [&](float qmax) {
-                qmax = __builtin_fmaxf(qmax, __shfl_xor(qmax, 32));   // lanes l and l ^ 32: the same head
-                int ex = 0;
-                if (qmax > 0.0f) (void)__builtin_frexpf(qmax, &ex);
-                const float qs = __builtin_ldexpf(1.0f, 14 - ex);     // qmax * qs < 2^14
-                score_mul = p.score_mul / qs;
-                return qs;
-            };
-            // read twice, for the maximum and for the conversion, so the
-            // fp32 fragment never occupies registers beside its fp16 form
-            float qmax = 0.0f;
+            const uint32_t qrow = Lq + (32 * hg + l32) * kQRow + 2 * (kHd * half + 8 * g);
 #pragma unroll
-            for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
-                    qmax = __builtin_fmaxf(qmax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                                                                 __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
-                }
-            const float qs = scale_of(qmax);
-#pragma unroll
-            for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const floatx4_t v = lds_ld<floatx4_t>(qf + 64 * ks + 16 * j);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = v[e] * qs;
-                        const _Float16 hi = (_Float16)x;
-                        qb[ks][4 * j + e] = hi;
-                        ql[ks][4 * j + e] = (_Float16)(x - (float)hi);
-                    }
-                }
+            for (int ks = 0; ks < kKs; ++ks) {
+                qb[ks] = lds_ld<half8_t>(qrow + 32 * ks);
+                ql[ks] = lds_ld<half8_t>(qrow + 2 * kD + 32 * ks);
+            }
+            score_mul = p.score_mul / q_scale[2 * (32 * hg + l32) + half];
             __syncthreads();                   // the first K tiles overwrite the staged queries
         }
 
