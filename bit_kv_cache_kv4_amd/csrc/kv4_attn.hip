@@ -16,17 +16,19 @@
 // into LDS) and P.V wavefronts 4..7 (quarter dq of the 512 latent dims:
 // O^T[128 dims x 64 heads] accumulated from V^T, read from the K tile itself
 // through ds_read_b64_tr_b16, and the P of all 64 heads).  A SIMD holds one
-// wavefront of each role.  LDS bandwidth bounds these loops on gfx950 as much
-// as the MFMA pipe (stores about 78 B/clk per CU, plain reads about 195 and
-// transposing reads about 92, measured); the roles let each V^T and P element
-// be read once per tile.
+// wavefront of each role, and the roles let each V^T and P element be read
+// once per tile.  At the LDS rates measured on gfx950 (stores about 78 B/clk
+// per CU, plain reads about 195, transposing reads about 92) the loops are
+// bound by the roles' instruction chains and the shared matrix pipe rather
+// than by LDS bandwidth.
 //
 // bf16 queries (sparse_mla_bf16_kernel): score wavefront = (head group hg =
 // w % 2 of 32 heads, row half rh = w / 2 of each tile) holds its heads' queries
 // over all dims and computes whole scores S^T[16 rows x 32 heads]
 // (v_mfma_f32_16x16x32_f16), so no partial scores are swapped and a tile takes
-// one barrier: scores and softmax of t + 1 beside the P.V of t, both roles
-// dequantizing t + 2 between their MFMAs.  fp32 queries (split into hi and lo
+// one barrier: scores and softmax of t + 1 beside the P.V of t, the score
+// wavefronts dequantizing their share of t + 2 between their MFMAs and the
+// P.V wavefronts theirs after their MFMAs.  fp32 queries (split into hi and lo
 // fp16 parts: twice the registers, sparse_mla_f32q_kernel): score wavefront =
 // (head group, half of the dims), partial scores S^T[32 rows x 32 heads]
 // (v_mfma_f32_32x32x16_f16) swapped with the partner half through LDS so each
