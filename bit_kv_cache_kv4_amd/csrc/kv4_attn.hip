@@ -179,8 +179,9 @@ __device__ __forceinline__ void load_pages(const AttnParams &p, const ListCtx &c
 }
 
 // Packs the valid entries' slots, in list order, to the front of slots[] and
-// pads with -1 up to a whole number of tile pairs (64 entries); returns the
-// number of valid entries (the same in every thread).  Holds a barrier, so every thread calls it; the caller
+// pads with -1 up to a whole number of tile pairs (64 entries, at least one
+// pair, so the first two tiles' entries are defined even for an empty list);
+// returns the number of valid entries (the same in every thread).  Holds a barrier, so every thread calls it; the caller
 // synchronizes before slots[] is read.
 __device__ __forceinline__ int pack_slots(const AttnParams &p, const ListCtx &c, const int32_t (&pos)[kPosPerLane],
                                           const int32_t (&phys)[kPosPerLane], int tid, int32_t *slots,
@@ -213,7 +214,7 @@ __device__ __forceinline__ int pack_slots(const AttnParams &p, const ListCtx &c,
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0u));
         if (sl[i] >= 0) slots[base[i] + below] = sl[i];
         const int e = tid + kThreads * i;
-        if (e >= nv && e < ((nv + 2 * kTile - 1) & ~(2 * kTile - 1))) slots[e] = -1;
+        if (e >= nv && e < max(2 * kTile, (nv + 2 * kTile - 1) & ~(2 * kTile - 1))) slots[e] = -1;
     }
     return nv;
 }
@@ -941,14 +942,15 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     uint32_t err = 0;
 
     // ---- Prologue.  Three dependent round trips (list entries, page-table
-    // entries, the first rows) come before the first tile.  The list goes
-    // out first, then this row's queries (74 KB: consecutive threads take
-    // consecutive 16-byte chunks of a head's row), then the page-table entries
-    // once the list is back; while those are in flight the queries are
-    // converted to fp16 and staged in LDS (in the third K tile and the P
-    // buffers, untouched until the first tile's softmax; rows padded by 16
-    // bytes), and the slot packing's barrier orders them before their
-    // readers.
+    // entries, the first rows) come before the first tile.  A wavefront's
+    // loads complete in issue order, so the page-table entries go out as
+    // soon as the list is back and before this row's queries (74 KB:
+    // consecutive threads take consecutive 16-byte chunks of a head's row);
+    // the slots are packed once the entries are back, the first two tiles'
+    // rows are gathered, and only then are the queries converted to fp16 and
+    // staged in LDS (in the third K tile and the P buffers, untouched until
+    // the first tile's softmax; rows padded by 16 bytes), while the rows are
+    // on their way.  A barrier orders the staged queries before their readers.
     constexpr int kQRow = kD * 2 + 16;
     constexpr int kQChunks = kD * 2 / 16;
     constexpr int kTPH = kThreads / 64;                    // threads per head row
@@ -1003,16 +1005,32 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     };
 
     load_positions(lc, e_lo, e_lo < e_hi ? first_hi : e_lo, tid, pos);
+    load_pages(p, lc, pos, phys);
+    __builtin_amdgcn_sched_barrier(0);             // the page-table loads issue before the query loads
     {
         const uint8_t *src = qr + (int64_t)min(h0 + q_hh, p.n_heads - 1) * p.q_head_stride * 2 + 16 * q_part;
 #pragma unroll
         for (int i = 0; i < kQPer; ++i) qc[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * kTPH * i);
     }
-    load_pages(p, lc, pos, phys);
-    stage_q();
+    __builtin_amdgcn_sched_barrier(0);
     int nv = __builtin_amdgcn_readfirstlane(pack_slots(p, lc, pos, phys, tid, slots, counts, err));
     if (tid == 0) *flag = 0;
     __syncthreads();
+    // the first two tiles' gathers, whether or not the list holds entries
+    // (skipped ones read the stand-in): a load count that does not depend on
+    // the list lets the query conversion wait for the queries alone; parts
+    // 0..7 (the score wavefronts') carry the rope
+    GSet<ROPE> G0, G1;
+    if (w < 4) {
+        gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+        gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+    } else {
+        gather_set<ROPE, false>(p.pool, stand_in, slots[gr], gp, G0);
+        gather_set<ROPE, false>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+    }
+    __builtin_amdgcn_sched_barrier(0);             // every gather out before the first wait on a query
+    stage_q();
+    __syncthreads();                               // queries staged
 
     const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
     int n_t = 0, n_real = 0, last_rows = kTile;
@@ -1061,12 +1079,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         // ================================================ score wavefronts
         const int hg = w & 1, rh = w >> 1;
         const int l16 = lane & 15, q4 = lane >> 4;
-        // parts 0..7 of a tile's rows, with the rope
-        GSet<ROPE> G0, G1;
-        if (nv > 0) {
-            gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
-            gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
-        }
 
         // k-step ks of lane group q4 covers chunk C(ks, q4) = 8 (ks / 2) +
         // 2 (ks % 2) + cq, cq = q4 / 2 + 4 (q4 % 2): the two 16-lane groups of
@@ -1283,14 +1295,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
         // ================================================ P.V wavefronts
         const int dq = w - 4;
         // parts 8..15 of a tile's rows, no rope
-        GSet<ROPE> G0, G1;
         auto gather_units = [&](int tile, GSet<ROPE> &G) {
             gather_set<ROPE, false>(p.pool, stand_in, slots[tile * kTile + gr], gp, G);
         };
-        if (nv > 0) {
-            gather_units(0, G0);
-            gather_units(1, G1);
-        }
 
         // transposing reads (A of O^T = V^T P^T), as in the fp32-query kernel
         const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), j4 = (lane >> 2) & 3;
