@@ -11,8 +11,16 @@
 // (atomic min), so "first occurrence" does not depend on the order in which
 // lanes win the race.  A lane keeps an entry iff its position is that
 // minimum.  The kept entries are placed by an exclusive prefix sum of per-lane
-// counts (wave scan with cross-lane reads, wave totals through LDS), staged in
-// LDS in list order and written out coalesced together with the -1 fill.
+// counts (within a wavefront from one ballot per item, the wavefronts' totals
+// through LDS), staged in LDS in list order and written out coalesced
+// together with the -1 fill.
+// With more lists than workgroups that fit on the chip at once, each
+// workgroup walks lists g, g + G, g + 2G, ... (G = the grid): the next
+// list's loads are issued before the current list is compacted, so their
+// round trip overlaps that work, and only the table slots a list used are
+// cleared before the next one.
+#include <hip/hip_runtime.h>
+
 #include "kv4_dedup_impl.h"
 #include "kv4_launch.h"
 
@@ -24,6 +32,63 @@ __global__ __launch_bounds__(THREADS) void dedup_kernel(const int32_t *__restric
                                                         int32_t *__restrict__ out_count, int log2_table) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     dedup_list<THREADS, ITEMS>(idx, k, idx_row_stride, out_idx, out_count, log2_table, blockIdx.x, lds);
+}
+
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void dedup_stream_kernel(const int32_t *__restrict__ idx, int32_t k,
+                                                               int64_t idx_row_stride, int32_t *__restrict__ out_idx,
+                                                               int32_t *__restrict__ out_count, int log2_table,
+                                                               int64_t n_lists) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    __builtin_assume(k > 0);                       // the launch takes this kernel only for k >= 1
+    const DedupLds<THREADS, ITEMS> m(lds, 1 << log2_table);
+    int64_t list = blockIdx.x;                     // < n_lists: the grid holds at most n_lists workgroups
+    int32_t ld[ITEMS];
+    dedup_load<THREADS, ITEMS>(idx + list * idx_row_stride, k, ld);
+    dedup_clear<THREADS, ITEMS>(m, 1 << log2_table);
+    dedup_stage<THREADS, ITEMS>(m, ld);
+    // Each list is staged at the end of the previous one's iteration, after
+    // that list's stores: the wait for its loads (issued before those stores)
+    // then leaves the stores in flight, which a wait at the loop's top, shared
+    // with the first list's, would not.
+    for (;;) {
+        const int64_t next = list + gridDim.x;
+        if (next < n_lists) dedup_load<THREADS, ITEMS>(idx + next * idx_row_stride, k, ld);   // uniform
+        __syncthreads();                           // list staged, table clear
+        int32_t v[ITEMS];
+        uint32_t slot[ITEMS];
+        dedup_core<THREADS, ITEMS>(m, k, log2_table, out_idx + list * (int64_t)k, out_count + list, v, slot);
+        if (next >= n_lists) break;
+        dedup_undo<THREADS, ITEMS>(m, v, slot);
+        __syncthreads();                           // stage read out before it takes the next list
+        dedup_stage<THREADS, ITEMS>(m, ld);
+        list = next;
+    }
+}
+
+// Workgroups of dedup_stream_kernel<THREADS, ITEMS> with `lds` bytes (a
+// function of the table size) that fit on the current device at once, 0 if
+// the runtime cannot say; looked up once per instance, device and table size.
+template <int THREADS, int ITEMS>
+static int64_t resident_workgroups(int log2_table, size_t lds) {
+    constexpr int kMaxDev = 64, kMaxLog2 = 32;
+    static int64_t cached[kMaxDev][kMaxLog2] = {};  // benign race: every caller stores the same value
+    const auto kernel = dedup_stream_kernel<THREADS, ITEMS>;
+    const int threads = THREADS;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const bool slot = dev >= 0 && dev < kMaxDev && log2_table >= 0 && log2_table < kMaxLog2;
+    if (slot && cached[dev][log2_table] > 0) return cached[dev][log2_table];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kernel), threads, lds) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int64_t n = (int64_t)per_cu * cus;
+    if (slot) cached[dev][log2_table] = n;
+    return n;
 }
 
 template <int THREADS, int ITEMS>
@@ -40,8 +105,24 @@ static hipError_t launch_dedup_items(const int32_t *idx, int64_t n_lists, int32_
             raised = true;
         }
     }
-    hipLaunchKernelGGL((dedup_kernel<THREADS, ITEMS>), dim3((unsigned)n_lists), dim3(THREADS), lds, stream, idx, k,
-                       stride, out_idx, out_count, log2_table);
+    auto stream_kernel = dedup_stream_kernel<THREADS, ITEMS>;
+    if (lds > 65536) {
+        static bool raised = false;   // benign race: every caller sets the same value
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(stream_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    const int64_t resident = resident_workgroups<THREADS, ITEMS>(log2_table, lds);
+    if (k > 0 && resident > 0 && n_lists > resident) {
+        hipLaunchKernelGGL(stream_kernel, dim3((unsigned)resident), dim3(THREADS), lds, stream, idx, k, stride, out_idx,
+                           out_count, log2_table, n_lists);
+    } else {
+        hipLaunchKernelGGL((dedup_kernel<THREADS, ITEMS>), dim3((unsigned)n_lists), dim3(THREADS), lds, stream, idx,
+                           k, stride, out_idx, out_count, log2_table);
+    }
     return hipGetLastError();
 }
 

@@ -34,74 +34,91 @@ inline int dedup_log2_table(int32_t k, int threads) {
     return l;
 }
 
-// Dedup of list `list` by a workgroup of THREADS lanes; lds holds
-// dedup_lds_words(THREADS, ITEMS, log2_table) 32-bit words, 16-byte aligned.
+// The table, the staged list and the scan's totals in LDS: dedup_lds_words
+// 32-bit words, 16-byte aligned.
 template <int THREADS, int ITEMS>
-__device__ __forceinline__ void dedup_list(const int32_t *__restrict__ idx, int32_t k, int64_t idx_row_stride,
-                                           int32_t *__restrict__ out_idx, int32_t *__restrict__ out_count,
-                                           int log2_table, int64_t list, uint32_t *lds) {
-    const int T = 1 << log2_table;
-    uint32_t *keys = lds;                    // T keys, then one private dummy slot per thread
-    int32_t *minpos = reinterpret_cast<int32_t *>(lds + T + THREADS);
-    int32_t *stage = reinterpret_cast<int32_t *>(lds + 2 * T + 2 * THREADS);
-    int32_t *wave_tot = stage + ITEMS * THREADS;
-    const int tid = threadIdx.x;
-    const int32_t *src = idx + list * idx_row_stride;
+struct DedupLds {
+    uint32_t *keys;       // T keys, then one private dummy slot per thread
+    int32_t *minpos;      // T smallest positions (and THREADS unused words)
+    int32_t *stage;       // ITEMS * THREADS entries: the list, then its kept entries
+    int32_t *wave_tot;    // per-wavefront counts of kept entries
+    __device__ DedupLds(uint32_t *lds, int T)
+        : keys(lds), minpos(reinterpret_cast<int32_t *>(lds + T + THREADS)),
+          stage(reinterpret_cast<int32_t *>(lds + 2 * T + 2 * THREADS)), wave_tot(stage + ITEMS * THREADS) {}
+};
 
-    {   // all of the list's loads in flight at once (k <= 256 * ITEMS), coalesced
-        int32_t ld[ITEMS];
+// the list's entries, coalesced: ld[i] = entry tid + THREADS i (-1 past k)
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_load(const int32_t *__restrict__ src, int32_t k, int32_t (&ld)[ITEMS]) {
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const int j = tid + THREADS * i;
-            ld[i] = j < k ? src[j] : -1;
-        }
-        for (int i = 4 * tid; i < T; i += 4 * THREADS) {   // T is a multiple of 4 * THREADS
-            *reinterpret_cast<uint4 *>(keys + i) = uint4{kEmpty, kEmpty, kEmpty, kEmpty};
-            *reinterpret_cast<int4 *>(minpos + i) = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
-        }
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) stage[tid + THREADS * i] = ld[i];
+    for (int i = 0; i < ITEMS; ++i) {
+        const int j = threadIdx.x + THREADS * i;
+        ld[i] = j < k ? src[j] : -1;
     }
-    __syncthreads();
+}
 
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_clear(const DedupLds<THREADS, ITEMS> &m, int T) {
+    for (int i = 4 * threadIdx.x; i < T; i += 4 * THREADS) {   // T is a multiple of 4 * THREADS
+        *reinterpret_cast<uint4 *>(m.keys + i) = uint4{kEmpty, kEmpty, kEmpty, kEmpty};
+        *reinterpret_cast<int4 *>(m.minpos + i) = int4{0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF};
+    }
+}
+
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_stage(const DedupLds<THREADS, ITEMS> &m, const int32_t (&ld)[ITEMS]) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) m.stage[threadIdx.x + THREADS * i] = ld[i];
+}
+
+// The dedup of a staged list (after a barrier that follows dedup_stage and
+// a cleared table): writes the k outputs and the count.  Leaves this
+// thread's entries v[] and their table slots slot[] (meaningful where
+// v[i] >= 0) for dedup_undo; every slot written with a key is one of them.
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_core(const DedupLds<THREADS, ITEMS> &m, int32_t k, int log2_table,
+                                           int32_t *__restrict__ dst, int32_t *__restrict__ count,
+                                           int32_t (&v)[ITEMS], uint32_t (&slot)[ITEMS]) {
+    const int T = 1 << log2_table;
+    const int tid = threadIdx.x;
     // Insert: every item's first compare-and-swap is issued before any result
     // is looked at (unconditionally: an entry < 0 targets this thread's dummy
     // slot, so no branch separates the atomics), then the few collisions probe
     // onwards, then the non-returning minimum of the positions.
-    int32_t v[ITEMS];
-    uint32_t slot[ITEMS];
     bool pending[ITEMS];
-    // stage holds -1 past k (written above for every entry of every thread)
+    // stage holds -1 past k (written by dedup_stage for every entry of every thread)
     if constexpr (ITEMS % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < ITEMS; i += 4) {
-            const int4 w = *reinterpret_cast<const int4 *>(stage + tid * ITEMS + i);
+            const int4 w = *reinterpret_cast<const int4 *>(m.stage + tid * ITEMS + i);
             v[i] = w.x, v[i + 1] = w.y, v[i + 2] = w.z, v[i + 3] = w.w;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) v[i] = stage[tid * ITEMS + i];
+        for (int i = 0; i < ITEMS; ++i) v[i] = m.stage[tid * ITEMS + i];
     }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
         slot[i] = v[i] >= 0 ? dedup_hash((uint32_t)v[i], log2_table) : (uint32_t)(T + tid);
     uint32_t old[ITEMS];
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) old[i] = lds_cas(&keys[slot[i]], kEmpty, (uint32_t)v[i]);
+    for (int i = 0; i < ITEMS; ++i) old[i] = lds_cas(&m.keys[slot[i]], kEmpty, (uint32_t)v[i]);
     __builtin_amdgcn_sched_barrier(0);        // all of them issued before any result is read
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) pending[i] = v[i] >= 0 && old[i] != kEmpty && old[i] != (uint32_t)v[i];
     // collisions: every pending item of the wavefront probes one slot further
-    // per round, all of a round's atomics issued together (the rest hit the
-    // thread's dummy slot), so the rounds number the longest probe, not the sum
+    // per round, all of a round's atomics issued together (only the pending
+    // lanes take part), so the rounds number the longest probe, not the sum
     bool any = false;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) any |= pending[i];
     while (__ballot(any) != 0) {
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            if (pending[i]) slot[i] = (slot[i] + 1) & (T - 1);
-            old[i] = lds_cas(&keys[pending[i] ? slot[i] : (uint32_t)(T + tid)], kEmpty, (uint32_t)v[i]);
+            if (pending[i]) {
+                slot[i] = (slot[i] + 1) & (T - 1);
+                old[i] = lds_cas(&m.keys[slot[i]], kEmpty, (uint32_t)v[i]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         any = false;
@@ -113,46 +130,85 @@ __device__ __forceinline__ void dedup_list(const int32_t *__restrict__ idx, int3
     }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
-        if (v[i] >= 0) lds_min(&minpos[slot[i]], tid * ITEMS + i);
+        if (v[i] >= 0) lds_min(&m.minpos[slot[i]], tid * ITEMS + i);
     __syncthreads();
 
+    // kept entries and their places: entry j = tid ITEMS + i is kept iff its
+    // position is its key's minimum; the kept entries of the wavefront's
+    // earlier lanes (all of whose entries precede this lane's) are counted
+    // from one ballot per item, the wavefronts' totals exchanged through LDS
     uint32_t keep = 0;
-    int cnt = 0;
+    int below = 0, wave_kept = 0;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-        const int j = tid * ITEMS + i;
-        if (v[i] >= 0 && minpos[slot[i]] == j) {
-            keep |= 1u << i;
-            ++cnt;
-        }
+        const bool k_i = v[i] >= 0 && m.minpos[slot[i]] == tid * ITEMS + i;
+        keep |= k_i ? 1u << i : 0u;
+        const uint64_t b = __ballot(k_i);
+        below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        wave_kept += (int)__popcll(b);
     }
-
-    // exclusive prefix sum of cnt over the workgroup, in lane order
     const int lane = tid & 63, wave = tid >> 6;
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
+    if (lane == 0) m.wave_tot[wave] = wave_kept;
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < THREADS / 64; ++w) {
-        const int t = wave_tot[w];
+        const int t = m.wave_tot[w];
         base += w < wave ? t : 0;
         total += t;
     }
-    int pos = base + incl - cnt;
+    int pos = base + below;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
-        if (keep & (1u << i)) stage[pos++] = v[i];   // stage was fully read before the barrier above
+        if (keep & (1u << i)) m.stage[pos++] = v[i];   // stage was fully read before the barrier above
     __syncthreads();
 
-    int32_t *dst = out_idx + list * (int64_t)k;
-    for (int j = tid; j < k; j += THREADS) dst[j] = j < total ? stage[j] : -1;
-    if (tid == 0) out_count[list] = total;
+    // ITEMS stores per thread on every path (k <= THREADS * ITEMS; lanes past
+    // k repeat entry k - 1's store, the same value to the same address): a
+    // caller that waits for loads issued before them can then leave the
+    // stores in flight, which a count that varies with the path would not
+    if (k > 0) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int j = min(tid + THREADS * i, k - 1);
+            dst[j] = j < total ? m.stage[j] : -1;
+        }
+    }
+    if (tid == 0) *count = total;
+}
+
+// Returns the table to its cleared state after dedup_core, touching only the
+// slots that hold keys (each is some thread's slot[i] with v[i] >= 0; the
+// dummy slots are never read).  The caller synchronizes after dedup_core's
+// last LDS read and before the next list's atomics.
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_undo(const DedupLds<THREADS, ITEMS> &m, const int32_t (&v)[ITEMS],
+                                           const uint32_t (&slot)[ITEMS]) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+        if (v[i] >= 0) {
+            m.keys[slot[i]] = kEmpty;
+            m.minpos[slot[i]] = 0x7FFFFFFF;
+        }
+}
+
+// Dedup of list `list` by a workgroup of THREADS lanes; lds holds
+// dedup_lds_words(THREADS, ITEMS, log2_table) 32-bit words, 16-byte aligned.
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_list(const int32_t *__restrict__ idx, int32_t k, int64_t idx_row_stride,
+                                           int32_t *__restrict__ out_idx, int32_t *__restrict__ out_count,
+                                           int log2_table, int64_t list, uint32_t *lds) {
+    const DedupLds<THREADS, ITEMS> m(lds, 1 << log2_table);
+    {   // all of the list's loads in flight at once (k <= THREADS * ITEMS), coalesced
+        int32_t ld[ITEMS];
+        dedup_load<THREADS, ITEMS>(idx + list * idx_row_stride, k, ld);
+        dedup_clear<THREADS, ITEMS>(m, 1 << log2_table);
+        dedup_stage<THREADS, ITEMS>(m, ld);
+    }
+    __syncthreads();
+    int32_t v[ITEMS];
+    uint32_t slot[ITEMS];
+    dedup_core<THREADS, ITEMS>(m, k, log2_table, out_idx + list * (int64_t)k, out_count + list, v, slot);
 }
 
 }  // namespace kv4

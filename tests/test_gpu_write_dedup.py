@@ -154,6 +154,27 @@ def test_dedup_lengths_and_edge_lists(k, L):
     assert (out_d == out_h).all()
 
 
+# More lists than workgroups fit on the chip at once: each workgroup compacts
+# several lists in turn, loading the next while it works and clearing only
+# the table slots the last one used.  Neighbouring lists differ in length of
+# distinct runs, so a slot left set would show in the next list's output.
+@pytest.mark.parametrize("k", [5, 300, 1000, 2048, 3000])
+def test_dedup_many_lists(k):
+    g = np.random.default_rng(50 + k)
+    L = 4100
+    idx = g.integers(-4, max(3, k // 2), size=(L, k)).astype(np.int32)
+    idx[0] = -1                                       # all padding
+    idx[1] = 7                                        # one value
+    idx[2] = np.arange(k, dtype=np.int32)             # all distinct
+    idx[3] = idx[2][::-1]
+    idx[L - 1] = g.integers(0, 2**31 - 1, size=k)     # large values, in the last (ragged) round
+    idx[L - 2] = -1
+    idx[1000::97] = np.arange(k, dtype=np.int32) % 3  # three values
+    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx)
+    assert (cnt_d == cnt_h).all()
+    assert (out_d == out_h).all()
+
+
 def test_dedup_strided_rows_and_prefix_k():
     g = np.random.default_rng(3)
     idx = g.integers(-2, 300, size=(50, 1000)).astype(np.int32)
