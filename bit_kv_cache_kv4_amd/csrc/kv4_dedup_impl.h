@@ -71,22 +71,11 @@ __device__ __forceinline__ void dedup_stage(const DedupLds<THREADS, ITEMS> &m, c
     for (int i = 0; i < ITEMS; ++i) m.stage[threadIdx.x + THREADS * i] = ld[i];
 }
 
-// The dedup of a staged list (after a barrier that follows dedup_stage and
-// a cleared table): writes the k outputs and the count.  Leaves this
-// thread's entries v[] and their table slots slot[] (meaningful where
-// v[i] >= 0) for dedup_undo; every slot written with a key is one of them.
+// This thread's entries tid ITEMS .. tid ITEMS + ITEMS - 1 from the staged
+// list (after a barrier that follows dedup_stage); stage holds -1 past k.
 template <int THREADS, int ITEMS>
-__device__ __forceinline__ void dedup_core(const DedupLds<THREADS, ITEMS> &m, int32_t k, int log2_table,
-                                           int32_t *__restrict__ dst, int32_t *__restrict__ count,
-                                           int32_t (&v)[ITEMS], uint32_t (&slot)[ITEMS]) {
-    const int T = 1 << log2_table;
+__device__ __forceinline__ void dedup_read_staged(const DedupLds<THREADS, ITEMS> &m, int32_t (&v)[ITEMS]) {
     const int tid = threadIdx.x;
-    // Insert: every item's first compare-and-swap is issued before any result
-    // is looked at (unconditionally: an entry < 0 targets this thread's dummy
-    // slot, so no branch separates the atomics), then the few collisions probe
-    // onwards, then the non-returning minimum of the positions.
-    bool pending[ITEMS];
-    // stage holds -1 past k (written by dedup_stage for every entry of every thread)
     if constexpr (ITEMS % 4 == 0) {
 #pragma unroll
         for (int i = 0; i < ITEMS; i += 4) {
@@ -97,6 +86,48 @@ __device__ __forceinline__ void dedup_core(const DedupLds<THREADS, ITEMS> &m, in
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) v[i] = m.stage[tid * ITEMS + i];
     }
+}
+
+// The same entries straight from the list, one vector load per four (or
+// fewer) of them; k must be a multiple of ITEMS (a thread's entries are all
+// in the list or all past it, then -1) and the list aligned to the vector.
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_load_direct(const int32_t *__restrict__ src, int32_t k, int32_t (&v)[ITEMS]) {
+    const int j0 = threadIdx.x * ITEMS;
+    const bool in = j0 < k;
+    const int32_t *p = src + (in ? j0 : 0);
+    if constexpr (ITEMS % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i += 4) {
+            int4 w = {-1, -1, -1, -1};
+            if (in) w = *reinterpret_cast<const int4 *>(p + i);
+            v[i] = w.x, v[i + 1] = w.y, v[i + 2] = w.z, v[i + 3] = w.w;
+        }
+    } else if constexpr (ITEMS == 2) {
+        int2 w = {-1, -1};
+        if (in) w = *reinterpret_cast<const int2 *>(p);
+        v[0] = w.x, v[1] = w.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) v[i] = in ? p[i] : -1;
+    }
+}
+
+// The dedup of a list whose entries v[] this thread holds (entries tid ITEMS
+// + i, -1 past k), the table cleared and synchronized: writes the k outputs
+// and the count.  Leaves the entries' table slots slot[] (meaningful where
+// v[i] >= 0) for dedup_undo; every slot written with a key is one of them.
+template <int THREADS, int ITEMS>
+__device__ __forceinline__ void dedup_core(const DedupLds<THREADS, ITEMS> &m, int32_t k, int log2_table,
+                                           int32_t *__restrict__ dst, int32_t *__restrict__ count,
+                                           const int32_t (&v)[ITEMS], uint32_t (&slot)[ITEMS]) {
+    const int T = 1 << log2_table;
+    const int tid = threadIdx.x;
+    // Insert: every item's first compare-and-swap is issued before any result
+    // is looked at (unconditionally: an entry < 0 targets this thread's dummy
+    // slot, so no branch separates the atomics), then the few collisions probe
+    // onwards, then the non-returning minimum of the positions.
+    bool pending[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
         slot[i] = v[i] >= 0 ? dedup_hash((uint32_t)v[i], log2_table) : (uint32_t)(T + tid);
@@ -208,6 +239,7 @@ __device__ __forceinline__ void dedup_list(const int32_t *__restrict__ idx, int3
     __syncthreads();
     int32_t v[ITEMS];
     uint32_t slot[ITEMS];
+    dedup_read_staged<THREADS, ITEMS>(m, v);
     dedup_core<THREADS, ITEMS>(m, k, log2_table, out_idx + list * (int64_t)k, out_count + list, v, slot);
 }
 

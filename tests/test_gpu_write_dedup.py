@@ -158,19 +158,23 @@ def test_dedup_lengths_and_edge_lists(k, L):
 # several lists in turn, loading the next while it works and clearing only
 # the table slots the last one used.  Neighbouring lists differ in length of
 # distinct runs, so a slot left set would show in the next list's output.
-@pytest.mark.parametrize("k", [5, 300, 1000, 2048, 3000])
-def test_dedup_many_lists(k):
-    g = np.random.default_rng(50 + k)
+# (k, row width): each thread's entries come straight from aligned rows when k
+# is a whole number of them (5, 300, 1000, 2048, 4096), through LDS otherwise
+# (1002 and 3000 are not; rows of 1001 are not aligned to 16 bytes)
+@pytest.mark.parametrize("k,width", [(5, 5), (300, 300), (1000, 1000), (1002, 1002), (1000, 1001), (2048, 2048),
+                                     (3000, 3000), (4096, 4096)])
+def test_dedup_many_lists(k, width):
+    g = np.random.default_rng(50 + k + width)
     L = 4100
-    idx = g.integers(-4, max(3, k // 2), size=(L, k)).astype(np.int32)
+    idx = g.integers(-4, max(3, k // 2), size=(L, width)).astype(np.int32)
     idx[0] = -1                                       # all padding
     idx[1] = 7                                        # one value
-    idx[2] = np.arange(k, dtype=np.int32)             # all distinct
-    idx[3] = idx[2][::-1]
-    idx[L - 1] = g.integers(0, 2**31 - 1, size=k)     # large values, in the last (ragged) round
+    idx[2, :k] = np.arange(k, dtype=np.int32)         # all distinct
+    idx[3, :k] = idx[2, :k][::-1]
+    idx[L - 1] = g.integers(0, 2**31 - 1, size=width)  # large values, in the last (ragged) round
     idx[L - 2] = -1
-    idx[1000::97] = np.arange(k, dtype=np.int32) % 3  # three values
-    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx)
+    idx[1000::97, :k] = np.arange(k, dtype=np.int32) % 3   # three values
+    out_d, cnt_d, out_h, cnt_h = _dedup_both(idx, k=k if width != k else None)
     assert (cnt_d == cnt_h).all()
     assert (out_d == out_h).all()
 
