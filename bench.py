@@ -650,7 +650,7 @@ def measure_ceilings(dev):
 
 def run_global_compact(name, pool, topk, pt, row_req, dev, reps=5):
     """Global dedup across all lists into a compacted pool: average time of a
-    HIP graph of `reps` calls (six kernels each); algorithmic bytes = the
+    HIP graph of `reps` calls (five to seven kernels each); algorithmic bytes = the
     lists read twice (marking, rewriting) and the rewritten lists written, the
     slot bitmap written and read twice, and the distinct rows read and
     written (page-table entries are not counted: they stay in L2)."""

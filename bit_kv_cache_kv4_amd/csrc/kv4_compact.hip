@@ -11,7 +11,9 @@
 // (when the bitmap fits in 64 KB, each workgroup into an LDS copy stored as a
 // partial bitmap, then OR-ed together; otherwise one global atomic per entry
 // into a cleared bitmap), scan it (per word, then per block of 4096 words,
-// then over the blocks), list U and rewrite the entries (a slot's index is
+// then over the blocks: inside the rewrite's workgroups when there are at
+// most 1024 blocks, else a launch of its own), list U and rewrite the
+// entries (a slot's index is
 // its block's base plus its word's base plus the set bits below it in the
 // word; for small bitmaps the rewrite is a launch of its own that reads the
 // word table from LDS), and copy the rows, one 16-byte piece per lane.
@@ -30,6 +32,8 @@ constexpr int kMarkParts = 512;                  // at most this many workgroups
 constexpr int kMarkPer = 32;                     // and entries per lane per round
 constexpr int kEmitPer = 4;                      // entries per lane when rewriting the lists
 constexpr int kLdsEmitWords = 8192;              // word tables up to 64 KB are read from LDS when rewriting
+constexpr int kInlineBlocks = 1024;              // up to this many scan blocks, each rewriting workgroup
+                                                 // scans the block totals itself (no launch of its own)
 
 // A query row's translation: through its page-table row, or physical slots
 // (no page table), or none at all (its request lies outside the table: every
@@ -207,7 +211,49 @@ __global__ __launch_bounds__(kCompactThreads) void compact_scan_kernel(const uin
     if (tid == 0) block_sum[blockIdx.x] = total;
 }
 
+// Exclusive prefix of the n_blocks (<= kInlineBlocks) block totals into
+// base[] (LDS) by the THREADS lanes of a workgroup, consecutive blocks per
+// lane; returns the total |U| in every lane.  Holds a barrier: every lane
+// calls it.
+template <int THREADS>
+__device__ __forceinline__ uint32_t block_prefix_lds(const uint32_t *__restrict__ block_sum, int32_t n_blocks,
+                                                     uint32_t *base, uint32_t *wave_tot) {
+    constexpr int kPer = kInlineBlocks / THREADS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t v[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = tid * kPer + i;
+        v[i] = b < n_blocks ? block_sum[b] : 0u;
+        sum += v[i];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    uint32_t run = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) {
+        run += w < wave ? wave_tot[w] : 0u;
+        total += wave_tot[w];
+    }
+    run += incl - sum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = tid * kPer + i;
+        if (b < n_blocks) base[b] = run;
+        run += v[i];
+    }
+    __syncthreads();
+    return total;
+}
+
 // one workgroup: exclusive prefix over the blocks, and the total |U|
+// (when there are more blocks than the rewriting workgroups scan themselves)
 __global__ __launch_bounds__(1024) void compact_top_kernel(const uint32_t *__restrict__ block_sum, int32_t n_blocks,
                                                            uint32_t *__restrict__ block_base,
                                                            int32_t *__restrict__ count) {
@@ -246,18 +292,31 @@ __global__ __launch_bounds__(1024) void compact_top_kernel(const uint32_t *__res
 
 // blocks [0, word_blocks): list U (lane per word, its set bits in order);
 // the rest: rewrite the entries, block word_blocks + b taking row b / chunks,
-// entries [kEmitPer * 256 (b % chunks), ...) of it, kEmitPer per lane
+// entries [kEmitPer * 256 (b % chunks), ...) of it, kEmitPer per lane.
+// INLINE: every workgroup first scans the n_blocks block totals into LDS (and
+// workgroup 0 writes |U|); otherwise block_base holds them, from
+// compact_top_kernel.
+template <bool INLINE>
 __global__ __launch_bounds__(kCompactThreads) void compact_emit_kernel(CompactParams p,
                                                                         const uint2 *__restrict__ word_info,
                                                                         int64_t n_words,
+                                                                        const uint32_t *__restrict__ block_sum,
+                                                                        int32_t n_blocks,
                                                                         const uint32_t *__restrict__ block_base,
                                                                         int64_t word_blocks, int32_t chunks,
                                                                         int32_t *__restrict__ uslots) {
+    __shared__ uint32_t s_base[INLINE ? kInlineBlocks : 1];
+    __shared__ uint32_t s_wave_tot[kCompactThreads / 64];
+    if constexpr (INLINE) {
+        const uint32_t total = block_prefix_lds<kCompactThreads>(block_sum, n_blocks, s_base, s_wave_tot);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *p.out_count = (int32_t)total;
+    }
+    auto base_of = [&](int64_t b) { return INLINE ? s_base[b] : block_base[b]; };
     if ((int64_t)blockIdx.x < word_blocks) {
         const int64_t w = (int64_t)blockIdx.x * kCompactThreads + threadIdx.x;
         if (w >= n_words) return;
         const uint2 wi = word_info[w];
-        uint32_t bits = wi.x, at = block_base[w / kScanWords] + wi.y;
+        uint32_t bits = wi.x, at = base_of(w / kScanWords) + wi.y;
         while (bits) {
             const int b = __builtin_ctz(bits);
             uslots[at++] = (int32_t)(w * 32 + b);
@@ -288,7 +347,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_emit_kernel(CompactPa
             const int64_t w = sl[v] >> 5;
             const uint2 wi = word_info[w];
             bits[v] = wi.x;
-            base[v] = block_base[w / kScanWords] + wi.y;
+            base[v] = base_of(w / kScanWords) + wi.y;
         }
     }
 #pragma unroll
@@ -302,15 +361,18 @@ __global__ __launch_bounds__(kCompactThreads) void compact_emit_kernel(CompactPa
 // LDS, since a gather from a table of a few thousand words touches dozens of
 // cache lines per wavefront.  Workgroup b takes rows [b * rows_per_part, ...),
 // a wavefront per row as in the marking.
+// A word's global base is the sum of the block totals before its block
+// (n_words <= kLdsEmitWords: at most two blocks).
 __global__ __launch_bounds__(kMarkThreads) void compact_emit_lds_kernel(CompactParams p,
                                                                          const uint2 *__restrict__ word_info,
                                                                          int64_t n_words,
-                                                                         const uint32_t *__restrict__ block_base,
+                                                                         const uint32_t *__restrict__ block_sum,
                                                                          int32_t rows_per_part) {
+    static_assert(kLdsEmitWords <= 2 * kScanWords, "more than two blocks to sum");
     extern __shared__ uint2 table[];
     for (int i = threadIdx.x; i < n_words; i += kMarkThreads) {
         uint2 wi = word_info[i];
-        wi.y += block_base[i / kScanWords];
+        if (i >= kScanWords) wi.y += block_sum[0];
         table[i] = wi;
     }
     __syncthreads();
@@ -414,18 +476,29 @@ hipError_t launch_global_compact(const CompactParams &p, void *workspace, hipStr
     if (w.n_blocks > 0)
         hipLaunchKernelGGL(compact_scan_kernel, dim3((unsigned)w.n_blocks), dim3(kCompactThreads), 0, stream, bitmap,
                            w.n_words, word_info, block_sum);
-    hipLaunchKernelGGL(compact_top_kernel, dim3(1), dim3(1024), 0, stream, block_sum, (int32_t)w.n_blocks, block_base,
-                       p.out_count);
+    // with few blocks the rewriting workgroups scan the block totals themselves
+    // (and the first writes |U|); otherwise one workgroup scans them first
+    const bool inline_base = w.n_blocks > 0 && w.n_blocks <= kInlineBlocks;
+    if (!inline_base)
+        hipLaunchKernelGGL(compact_top_kernel, dim3(1), dim3(1024), 0, stream, block_sum, (int32_t)w.n_blocks,
+                           block_base, p.out_count);
     const int64_t word_blocks = (w.n_words + kCompactThreads - 1) / kCompactThreads;
     const int32_t chunks = (p.k + kEmitPer * kCompactThreads - 1) / (kEmitPer * kCompactThreads);
     const bool lds_emit = w.n_parts > 0 && w.n_words <= kLdsEmitWords;
     const int64_t entry_blocks = n_entries > 0 && !lds_emit ? (int64_t)p.n_rows * chunks : 0;
     if (lds_emit)
         hipLaunchKernelGGL(compact_emit_lds_kernel, dim3((unsigned)w.n_parts), dim3(kMarkThreads),
-                           (size_t)w.n_words * 8, stream, p, word_info, w.n_words, block_base, w.rows_per_part);
-    if (word_blocks + entry_blocks > 0)
-        hipLaunchKernelGGL(compact_emit_kernel, dim3((unsigned)(word_blocks + entry_blocks)), dim3(kCompactThreads), 0,
-                           stream, p, word_info, w.n_words, block_base, word_blocks, chunks, uslots);
+                           (size_t)w.n_words * 8, stream, p, word_info, w.n_words, block_sum, w.rows_per_part);
+    if (word_blocks + entry_blocks > 0) {
+        if (inline_base)
+            hipLaunchKernelGGL(compact_emit_kernel<true>, dim3((unsigned)(word_blocks + entry_blocks)),
+                               dim3(kCompactThreads), 0, stream, p, word_info, w.n_words, block_sum,
+                               (int32_t)w.n_blocks, block_base, word_blocks, chunks, uslots);
+        else
+            hipLaunchKernelGGL(compact_emit_kernel<false>, dim3((unsigned)(word_blocks + entry_blocks)),
+                               dim3(kCompactThreads), 0, stream, p, word_info, w.n_words, block_sum,
+                               (int32_t)w.n_blocks, block_base, word_blocks, chunks, uslots);
+    }
     if (w.max_rows > 0) {
         const int64_t pieces = w.max_rows * (p.row_bytes / 16);
         const unsigned copy_blocks = (unsigned)std::min<int64_t>(16384, (pieces + kCompactThreads - 1) / kCompactThreads);

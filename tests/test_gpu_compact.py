@@ -55,6 +55,41 @@ def test_compact_physical_slots(n_slots, R, k):
     _both(pool_h, topk, pool_d=pool_d)
 
 
+def test_compact_pool_past_the_inline_scan():
+    """A pool of 140M slots: more than 1024 scan blocks of 4096 bitmap words,
+    so the block totals get a scan launch of their own before the rewrite
+    (smaller pools scan them inside it).  The compaction depends only on the
+    order of the distinct slots, so the oracle runs on the same lists with
+    their slots renumbered in order onto a small pool holding the same rows;
+    entries past the pool map past the small one (flagged by both)."""
+    n_slots = 140_000_000
+    g = np.random.default_rng(140)
+    R, k = 3, 700
+    used = np.unique(g.integers(0, n_slots, size=1500))
+    used = np.union1d(used, [0, 134_217_727, 134_217_728, n_slots - 1])   # both sides of block 1024, the ends
+    topk = g.choice(used, size=(R, k)).astype(np.int64)
+    topk[0, :6] = [n_slots - 1, n_slots, n_slots + 7, -1, 134_217_728, 0]
+    topk[2] = -1
+    valid = (topk >= 0) & (topk < n_slots)
+    small = np.where(valid, np.searchsorted(used, np.clip(topk, 0, n_slots - 1)),
+                     np.where(topk >= n_slots, len(used) + (topk - n_slots), topk)).astype(np.int32)
+    rows = g.integers(0, 256, size=(len(used), 352)).astype(np.uint8)
+    cp_h, idx_h, n_h, err_h = oracle.global_compact(small, rows)
+    pool_d = torch.empty((n_slots, 352), dtype=torch.uint8, device=DEV)
+    pool_d[torch.from_numpy(used).to(DEV)] = to_dev(rows)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    cp_d, idx_d, n_d = kv4.global_compact(pool_d, to_dev(topk.astype(np.int32)), err_word=err)
+    torch.cuda.synchronize()
+    n = int(n_d.item())
+    try:
+        assert n == n_h and int(err.item()) == err_h
+        assert (idx_d.cpu().numpy() == idx_h).all()
+        assert (cp_d[:n].cpu().numpy() == cp_h).all()
+    finally:
+        del pool_d, cp_d
+        torch.cuda.empty_cache()
+
+
 def test_compact_all_invalid():
     pool = np.zeros((100, 352), np.uint8)
     topk = np.full((4, 16), -1, np.int32)
