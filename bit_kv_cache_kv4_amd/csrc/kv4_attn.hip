@@ -946,11 +946,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     // loads complete in issue order, so the page-table entries go out as
     // soon as the list is back and before this row's queries (74 KB:
     // consecutive threads take consecutive 16-byte chunks of a head's row);
-    // the slots are packed once the entries are back, the first two tiles'
-    // rows are gathered, and only then are the queries converted to fp16 and
+    // the slots are packed once the entries are back, the first tile's rows
+    // are gathered, and only then are the queries converted to fp16 and
     // staged in LDS (in the third K tile and the P buffers, untouched until
     // the first tile's softmax; rows padded by 16 bytes), while the rows are
-    // on their way.  A barrier orders the staged queries before their readers.
+    // on their way; then the second tile's rows are gathered.  A barrier
+    // orders the staged queries before their readers.
     constexpr int kQRow = kD * 2 + 16;
     constexpr int kQChunks = kD * 2 / 16;
     constexpr int kTPH = kThreads / 64;                    // threads per head row
@@ -1018,18 +1019,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
     __syncthreads();
     // the first two tiles' gathers, whether or not the list holds entries
     // (skipped ones read the stand-in): a load count that does not depend on
-    // the list lets the query conversion wait for the queries alone; parts
-    // 0..7 (the score wavefronts') carry the rope
+    // the list lets the query conversion wait for the queries alone.  Tile
+    // 0's go out before the conversion and tile 1's after it, so the first
+    // burst of row fetches is one tile per workgroup (tile 1 is converted
+    // after tile 0's scores).  Parts 0..7 (the score wavefronts') carry the
+    // rope.
     GSet<ROPE> G0, G1;
-    if (w < 4) {
-        gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
-        gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
-    } else {
-        gather_set<ROPE, false>(p.pool, stand_in, slots[gr], gp, G0);
-        gather_set<ROPE, false>(p.pool, stand_in, slots[kTile + gr], gp, G1);
-    }
-    __builtin_amdgcn_sched_barrier(0);             // every gather out before the first wait on a query
+    if (w < 4) gather_set<ROPE>(p.pool, stand_in, slots[gr], gp, G0);
+    else gather_set<ROPE, false>(p.pool, stand_in, slots[gr], gp, G0);
+    __builtin_amdgcn_sched_barrier(0);             // tile 0's gathers out before the first wait on a query
     stage_q();
+    __builtin_amdgcn_sched_barrier(0);
+    if (w < 4) gather_set<ROPE>(p.pool, stand_in, slots[kTile + gr], gp, G1);
+    else gather_set<ROPE, false>(p.pool, stand_in, slots[kTile + gr], gp, G1);
     __syncthreads();                               // queries staged
 
     const uint32_t K0 = L, K1 = L + kKTileB, K2 = L + 2 * kKTileB;
@@ -1225,9 +1227,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 }
                 dequant_set<ROPE>(K0, gr, gp, true, G0);
                 gather_set<ROPE>(p.pool, stand_in, slots[min(2, n_t - 1) * kTile + gr], gp, G0);
-                dequant_set<ROPE>(K1, gr, gp, true, G1);
-                gather_set<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, G1);
-                __syncthreads();                   // tiles 0 and 1 in LDS
+                __syncthreads();                   // tile 0 in LDS (tile 1 follows, under its scores)
                 {
                     floatx4_t acc[2];
                     scores(K0, acc);
@@ -1251,7 +1251,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                     }
                     softmax(acc, tile_lim(0), 0);
                 }
-                __syncthreads();                   // P of tile 0 in P buffer 0
+                dequant_set<ROPE>(K1, gr, gp, true, G1);
+                gather_set<ROPE>(p.pool, stand_in, slots[min(3, n_t - 1) * kTile + gr], gp, G1);
+                __syncthreads();                   // P of tile 0 in P buffer 0, tile 1 in LDS
                 uint32_t bA = K0, bB = K1, bC = K2;
                 for (int t = 0; t < n_t; t += 2) {
                     iteration(t, G0, bB, bC);      // G0: tile t + 2 -> bC, then t + 4
@@ -1366,14 +1368,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
                 }
                 dequant_set<ROPE>(K0, gr, gp, false, G0);
                 gather_units(min(2, n_t - 1), G0);
-                dequant_set<ROPE>(K1, gr, gp, false, G1);
+                __syncthreads();                   // tile 0 in LDS
+                dequant_set<ROPE>(K1, gr, gp, false, G1);   // while tile 0 is scored
                 gather_units(min(3, n_t - 1), G1);
-                __syncthreads();                   // tiles 0 and 1 in LDS
                 if (!have_ref) {
                     __syncthreads();               // the reference is agreed
                     have_ref = true;
                 }
-                __syncthreads();                   // P of tile 0 in P buffer 0
+                __syncthreads();                   // P of tile 0 in P buffer 0, tile 1 in LDS
                 uint32_t bA = K0, bB = K1, bC = K2;
                 for (int t = 0; t < n_t; t += 2) {
                     iteration(t, G0, bA, bC);
