@@ -315,6 +315,12 @@ def main():
     pool, pt, sets = wl["pool"], wl["pt"], wl["sets"]
     H, R, K = spec.n_heads, spec.n_req, spec.k
     S = args.splits or kv4.sparse_mla_decode_splits(sets[0]["q"], pool, sets[0]["topk"], page_table=pt)
+    # the decode workspace, allocated once up front as an engine would at
+    # start-up (a workspace allocated after the other buffers made the same
+    # steps 0.6-0.9 us slower in one measurement: the placement of the
+    # allocation, not the kernels, which are the same)
+    ws = torch.empty(max(1, kv4.sparse_mla_decode_workspace(sets[0]["q"], pool, sets[0]["topk"], S, page_table=pt)),
+                     dtype=torch.uint8, device=dev)
     part_o = torch.empty((S, R, H, 512), dtype=torch.float16, device=dev)   # as decode's workspace holds them
     part_lse = torch.empty((S, R, H), dtype=torch.float32, device=dev)
     out = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
@@ -327,12 +333,10 @@ def main():
         st = sets[i % len(sets)]
         # the new rows' write and the lists' compaction: one call, one kernel
         kv4.write_and_dedup(st["new_rows"], wl["new_slots"], pool, st["topk"], out_idx=lists, out_count=counts)
-        if S > 1:
-            kv4.sparse_mla_decode_partial(st["q"], pool, lists, spec.sm_scale, S, page_table=pt,
-                                          part_o=part_o, part_lse=part_lse)
-            kv4.merge_states(part_o, part_lse, out=out, lse=lse)
-        else:
-            kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=1, out=out, lse=lse)
+        # the decode call: the split kernel (fp16 parts in the workspace) and
+        # the merge, which takes each row's parts on the XCD that wrote them
+        kv4.sparse_mla_decode(st["q"], pool, lists, spec.sm_scale, page_table=pt, num_splits=S, workspace=ws,
+                              out=out, lse=lse)
 
     # The timed steps run from HIP graphs that hold one step per rotating
     # input set, in order (a step's three calls are launched by the GPU, not

@@ -431,6 +431,10 @@ kv4_status kv4_sparse_mla_decode(const kv4_attn_args *a, int32_t num_splits, voi
     m.out_row_stride = a->out_row_stride;
     m.out_col_stride = KV4_LATENT;
     m.lse = a->lse;
+    // the split kernel's workgroup (r, s, z) has linear index r + n_rows (s +
+    // S z); dealt round-robin over the 8 XCDs, every split of row r then runs
+    // on XCD r % 8 when n_rows is a multiple of 8
+    m.xcd_group = a->n_rows % 8 == 0 ? a->n_heads : 0;
     return hip_status(kv4::launch_merge_states(m, (hipStream_t)stream), "merge_states launch");
 }
 

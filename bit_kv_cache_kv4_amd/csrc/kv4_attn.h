@@ -50,6 +50,12 @@ struct MergeParams {
     float *out;                // (t, d) at (t / spr) * out_row_stride + (t % spr) * out_col_stride + d
     int64_t out_row_stride, out_col_stride;
     float *lse;                // (t) at t, nullable
+    // Placement hint, 0 for none: the states come in groups of this many
+    // consecutive ones, group g's parts written by workgroups on XCD g % 8
+    // (the split kernel's rows when their count is a multiple of 8).  The
+    // merge then takes each group on that XCD, where the parts may still
+    // sit in L2.  Only the order of the work depends on it.
+    int64_t xcd_group;
 };
 
 hipError_t launch_merge_states(const MergeParams &p, hipStream_t stream);

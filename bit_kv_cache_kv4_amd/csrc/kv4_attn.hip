@@ -1591,12 +1591,28 @@ __device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, i
 }
 
 // wavefronts take tasks in order, the grid's wavefronts apart
+// Workgroup b takes tasks [kMergeWaves v, +kMergeWaves), v = b unless the
+// placement hint applies (one pass over whole groups of states, a whole number
+// of workgroups per group, groups a multiple of 8): then workgroup b, dealt to
+// XCD b % 8, takes the groups g = b % 8 (mod 8), so it reads the parts that
+// workgroups on its own XCD wrote.
+__device__ __forceinline__ int64_t merge_block(const MergeParams &p, int n_seg) {
+    const int64_t b = blockIdx.x;
+    if (p.xcd_group <= 0 || p.n_states % (8 * p.xcd_group)) return b;
+    const int64_t per_group = p.xcd_group * n_seg;          // tasks of a group
+    if (per_group % kMergeWaves) return b;
+    const int64_t wg_per_group = per_group / kMergeWaves;
+    if ((int64_t)gridDim.x != (p.n_states / p.xcd_group) * wg_per_group) return b;
+    const int64_t j = b / 8;
+    return (8 * (j / wg_per_group) + b % 8) * wg_per_group + j % wg_per_group;
+}
+
 template <bool F16, int B>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_states_kernel(MergeParams p) {
     const int n_seg = (p.dim + kMergeSeg - 1) / kMergeSeg;
     const int64_t tasks = p.n_states * n_seg;
     const int64_t stride = (int64_t)gridDim.x * kMergeWaves;
-    for (int64_t task = (int64_t)blockIdx.x * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t task = merge_block(p, n_seg) * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
          task < tasks; task += stride)
         merge_task<F16, B>(p, task, n_seg, threadIdx.x & 63);
 }
