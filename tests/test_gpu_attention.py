@@ -159,6 +159,18 @@ def test_head_counts(h):
     _run(spec, W.queries(spec), W.topk_lists(spec), W.page_table(spec), prefill=True)
 
 
+# Rows a multiple of 8: the decode's merge takes each row on the XCD that
+# wrote its parts (a reordering of its work only); 48 and 80 heads give
+# groups of states that are not powers of two, 128 heads two head blocks.
+@pytest.mark.parametrize("h", [48, 80, 128])
+@pytest.mark.parametrize("rows", [8, 16])
+def test_decode_rows_multiple_of_eight(h, rows):
+    spec = W.scaled(SMALL, n_req=rows, n_heads=h, n_pool_pages=rows * 40)
+    q, topk, pt = W.queries(spec), W.topk_lists(spec), W.page_table(spec)
+    for s in (0, 3, 5):
+        _run(spec, q, topk, pt, num_splits=s)
+
+
 def test_fp32_queries():
     spec = W.scaled(SMALL, q_dtype="f32")
     q = W.queries(spec)
