@@ -477,8 +477,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_f32q_kernel(AttnParams p)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int pj = 64 * j + (tid & 63);
-                    if (hh < n_live)
-                        *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)) = lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj);
+                    if (hh < n_live)   // the final fp32 output, non-temporal (prefill 1% faster)
+                        __builtin_nontemporal_store(lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj),
+                                                    reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)));
                 }
             }
         }
@@ -1070,8 +1071,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_bf16_kernel(AttnParams p)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int pj = 64 * j + (tid & 63);
-                    if (hh < n_live)
-                        *reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)) = lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj);
+                    if (hh < n_live)   // the final fp32 output, non-temporal (prefill 1% faster)
+                        __builtin_nontemporal_store(lds_ld<floatx4_t>(L + hh * kORowF + 16 * pj),
+                                                    reinterpret_cast<floatx4_t *>(ob + (hh * kLatent + 4 * pj)));
                 }
             }
         }
@@ -1587,7 +1589,9 @@ __device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, i
         }
     }
     float *orow = p.out + (t / p.states_per_row) * p.out_row_stride + (t % p.states_per_row) * p.out_col_stride;
-    if (live) *reinterpret_cast<floatx4_t *>(orow + d) = acc * inv;
+    // non-temporal: the result is not read again here, and keeping it out of
+    // L2 spares the write-back at the kernel's end (C3 step 1% faster)
+    if (live) __builtin_nontemporal_store(acc * inv, reinterpret_cast<floatx4_t *>(orow + d));
 }
 
 // wavefronts take tasks in order, the grid's wavefronts apart
