@@ -225,21 +225,25 @@ __device__ __forceinline__ void dedup_undo(const DedupLds<THREADS, ITEMS> &m, co
 
 // Dedup of list `list` by a workgroup of THREADS lanes; lds holds
 // dedup_lds_words(THREADS, ITEMS, log2_table) 32-bit words, 16-byte aligned.
-template <int THREADS, int ITEMS>
+template <int THREADS, int ITEMS, bool DIRECT = false>
 __device__ __forceinline__ void dedup_list(const int32_t *__restrict__ idx, int32_t k, int64_t idx_row_stride,
                                            int32_t *__restrict__ out_idx, int32_t *__restrict__ out_count,
                                            int log2_table, int64_t list, uint32_t *lds) {
     const DedupLds<THREADS, ITEMS> m(lds, 1 << log2_table);
-    {   // all of the list's loads in flight at once (k <= THREADS * ITEMS), coalesced
+    int32_t v[ITEMS];
+    if constexpr (DIRECT) {
+        dedup_load_direct<THREADS, ITEMS>(idx + list * idx_row_stride, k, v);
+        dedup_clear<THREADS, ITEMS>(m, 1 << log2_table);
+        __syncthreads();
+    } else {   // all of the list's loads in flight at once (k <= THREADS * ITEMS), coalesced
         int32_t ld[ITEMS];
         dedup_load<THREADS, ITEMS>(idx + list * idx_row_stride, k, ld);
         dedup_clear<THREADS, ITEMS>(m, 1 << log2_table);
         dedup_stage<THREADS, ITEMS>(m, ld);
+        __syncthreads();
+        dedup_read_staged<THREADS, ITEMS>(m, v);
     }
-    __syncthreads();
-    int32_t v[ITEMS];
     uint32_t slot[ITEMS];
-    dedup_read_staged<THREADS, ITEMS>(m, v);
     dedup_core<THREADS, ITEMS>(m, k, log2_table, out_idx + list * (int64_t)k, out_count + list, v, slot);
 }
 

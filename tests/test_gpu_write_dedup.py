@@ -217,6 +217,8 @@ def _write_and_dedup_both(kv, slots, n_slots, idx, k=None):
     (70, 0, 16),         # write only
     (33, 5, 4096),       # longest lists
     (17, 300, 700),      # enough lists for the two separate kernels
+    (9, 20, 1025),       # two entries a thread, k odd: staged through LDS
+    (9, 20, 2051),       # four entries a thread, k not a multiple of four
 ])
 def test_write_and_dedup_equals_oracle(n_tokens, n_lists, k):
     g = np.random.default_rng(1000 + n_tokens + n_lists + k)
@@ -231,6 +233,26 @@ def test_write_and_dedup_equals_oracle(n_tokens, n_lists, k):
     _assert_same_bytes(got, want)
     assert e_d == e_h
     assert (cnt_d == cnt_h).all() and (out_d == out_h).all()
+
+
+@pytest.mark.parametrize("k", [700, 1500, 3000])
+def test_write_and_dedup_unaligned_lists(k):
+    """Lists that start one entry into a device buffer, so that a thread's
+    entries are not one aligned vector: the staged load path."""
+    g = np.random.default_rng(77 + k)
+    kv = g.standard_normal((12, 576)).astype(np.float32)
+    slots = g.permutation(64)[:12].astype(np.int32)
+    idx = g.integers(-2, k // 4, size=(9, k)).astype(np.int32)
+    pool_h = np.full((64, 352), 0xA5, np.uint8)
+    oracle.quant_write(kv, slots, pool_h)
+    out_h, cnt_h = oracle.dedup_compact(idx)
+    wide = torch.zeros((9, k + 1), dtype=torch.int32, device=DEV)
+    wide[:, 1:] = to_dev(idx)
+    pool_d = torch.full((64, 352), 0xA5, dtype=torch.uint8, device=DEV)
+    out_d, cnt_d = kv4.write_and_dedup(to_dev(kv), to_dev(slots), pool_d, wide[:, 1:])
+    torch.cuda.synchronize()
+    _assert_same_bytes(pool_d.cpu().numpy(), pool_h)
+    assert (cnt_d.cpu().numpy() == cnt_h).all() and (out_d.cpu().numpy() == out_h).all()
 
 
 def test_write_and_dedup_prefix_k_and_step_inputs():
