@@ -1511,16 +1511,22 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 
 // ----------------------------------------------------------------- merge
 
-// One wavefront per state t and 256 dims of it; a lane owns 4 consecutive
-// dims.  Lane s loads part s's lse (at most 64 parts) and computes its weight;
+// One wavefront per state t and 256 dims of it, a lane owning 4 consecutive
+// dims, or 512 (W = 2 pieces of 4 per lane) when the grid has wavefronts to
+// spare: half the wavefronts, each with twice the loads in flight.  Lane s loads part s's lse (at most 64 parts) and computes its weight;
 // the lanes read the maximum, the weights and their sum across the wavefront,
 // so there is no LDS and no barrier.  With at most 32 parts (decode's case) the
 // parts' o are loaded together with the lse, one round trip for all.  With M the
 // largest lse: w_s = exp(lse_s - M) (an empty part weighs 0), W = the w_s
 // summed in part order, o = (the w_s o_s summed in part order) / W, lse = M +
 // ln W; all parts empty gives o = 0, lse = -inf.
-constexpr int kMergeSeg = 256;                 // dims per wavefront
+constexpr int kMergeSeg = 256;                 // dims per wavefront and piece per lane
 constexpr int kMergeWaves = 4;                 // wavefronts per workgroup
+// at least this many 256-dim tasks (16 wavefronts per CU) and at most 8 parts:
+// 512 dims per wavefront.  Measured: the long-context decode step's merge
+// (4096 states, 4 parts) 0.4 us faster; 8 requests x 64 heads with 16 parts
+// (1024 tasks) 1 us slower.
+constexpr int64_t kWideMergeTasks = 4096;
 
 // four consecutive dims of one part's o as stored (fp16 parts stay fp16 until
 // used), and widened to fp32 (exact)
@@ -1537,26 +1543,34 @@ __device__ __forceinline__ floatx4_t widen(PartPiece<F16> x) {
     else return x;
 }
 
-// task = (state t, segment of 256 dims) for the calling wavefront.  B > 0:
-// at most B parts, all loaded before any is used (a part past the last
-// re-reads the last; it is not used); B = 0: any count, loaded as used.
-template <bool F16, int B>
+// task = (state t, segment of 256 W dims) for the calling wavefront; the lane
+// owns dims d + 4j (j < W).  B > 0: at most B parts, all loaded before any is
+// used (a part past the last re-reads the last; it is not used); B = 0: any
+// count, loaded as used.
+template <bool F16, int B, int W>
 __device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, int n_seg, int lane) {
     const int64_t t = task / n_seg;
     const int seg = (int)(task - t * n_seg);
-    const int d = seg * kMergeSeg + 4 * lane;
-    const bool live = d < p.dim;
+    const int d = seg * kMergeSeg * W + 4 * W * lane;
     const int S = p.n_parts;
-    const int64_t o_t = t * p.dim + (live ? d : 0);            // part s at s * n_states * dim
+    bool live[W];
+    int64_t o_t[W];                                             // part s at s * n_states * dim
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        live[j] = d + 4 * j < p.dim;
+        o_t[j] = t * p.dim + (live[j] ? d + 4 * j : 0);
+    }
     const int64_t o_stride = p.n_states * (int64_t)p.dim;
     // lane s holds part s's lse and, once M is known, its weight; every lane
     // reads them from there in part order
     // (no load sits under a branch, so none waits for another)
     const float my_raw = p.part_lse[t + (int64_t)min(lane, S - 1) * p.n_states];
-    PartPiece<F16> v[B > 0 ? B : 1];
+    PartPiece<F16> v[B > 0 ? B : 1][W];
     if constexpr (B > 0) {
 #pragma unroll
-        for (int s = 0; s < B; ++s) v[s] = load_piece<F16>(p, o_t + min(s, S - 1) * o_stride);
+        for (int s = 0; s < B; ++s)
+#pragma unroll
+            for (int j = 0; j < W; ++j) v[s][j] = load_piece<F16>(p, o_t[j] + min(s, S - 1) * o_stride);
     }
     const float my = lane < S ? my_raw : -__builtin_inff();
     auto lane_val = [](float x, int s) {
@@ -1566,32 +1580,40 @@ __device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, i
     for (int s = 0; s < S; ++s) M = __builtin_fmaxf(M, lane_val(my, s));
     const float my_w = my == -__builtin_inff() || M == -__builtin_inff() ? 0.0f : expf(my - M);
     auto weight = [&](int s) { return lane_val(my_w, s); };
-    float W = 0.0f;
+    float Wsum = 0.0f;
     if (M != -__builtin_inff())
-        for (int s = 0; s < S; ++s) W += weight(s);
-    if (seg == 0 && lane == 0 && p.lse) p.lse[t] = M == -__builtin_inff() ? M : M + logf(W);
-    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-    floatx4_t acc = {0, 0, 0, 0};
-    if (W > 0.0f) {
+        for (int s = 0; s < S; ++s) Wsum += weight(s);
+    if (seg == 0 && lane == 0 && p.lse) p.lse[t] = M == -__builtin_inff() ? M : M + logf(Wsum);
+    const float inv = Wsum > 0.0f ? 1.0f / Wsum : 0.0f;
+    floatx4_t acc[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) acc[j] = floatx4_t{0, 0, 0, 0};
+    if (Wsum > 0.0f) {
         if constexpr (B > 0) {
 #pragma unroll
             for (int s = 0; s < B; ++s) {
                 if (s < S) {
                     const float ws = weight(s);
-                    if (ws != 0.0f) acc += ws * widen<F16>(v[s]);
+                    if (ws != 0.0f)
+#pragma unroll
+                        for (int j = 0; j < W; ++j) acc[j] += ws * widen<F16>(v[s][j]);
                 }
             }
         } else {
             for (int s = 0; s < S; ++s) {
                 const float ws = weight(s);
-                if (ws != 0.0f) acc += ws * widen<F16>(load_piece<F16>(p, o_t + s * o_stride));
+                if (ws != 0.0f)
+#pragma unroll
+                    for (int j = 0; j < W; ++j) acc[j] += ws * widen<F16>(load_piece<F16>(p, o_t[j] + s * o_stride));
             }
         }
     }
     float *orow = p.out + (t / p.states_per_row) * p.out_row_stride + (t % p.states_per_row) * p.out_col_stride;
     // non-temporal: the result is not read again here, and keeping it out of
     // L2 spares the write-back at the kernel's end (C3 step 1% faster)
-    if (live) __builtin_nontemporal_store(acc * inv, reinterpret_cast<floatx4_t *>(orow + d));
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+        if (live[j]) __builtin_nontemporal_store(acc[j] * inv, reinterpret_cast<floatx4_t *>(orow + d + 4 * j));
 }
 
 // wavefronts take tasks in order, the grid's wavefronts apart
@@ -1611,32 +1633,36 @@ __device__ __forceinline__ int64_t merge_block(const MergeParams &p, int n_seg) 
     return (8 * (j / wg_per_group) + b % 8) * wg_per_group + j % wg_per_group;
 }
 
-template <bool F16, int B>
+template <bool F16, int B, int W>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_states_kernel(MergeParams p) {
-    const int n_seg = (p.dim + kMergeSeg - 1) / kMergeSeg;
+    const int n_seg = (p.dim + kMergeSeg * W - 1) / (kMergeSeg * W);
     const int64_t tasks = p.n_states * n_seg;
     const int64_t stride = (int64_t)gridDim.x * kMergeWaves;
     for (int64_t task = merge_block(p, n_seg) * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
          task < tasks; task += stride)
-        merge_task<F16, B>(p, task, n_seg, threadIdx.x & 63);
+        merge_task<F16, B, W>(p, task, n_seg, threadIdx.x & 63);
 }
 
 template <bool F16>
-void launch_merge(const MergeParams &p, dim3 grid, dim3 block, hipStream_t stream) {
-    if (p.n_parts <= 4) hipLaunchKernelGGL((merge_states_kernel<F16, 4>), grid, block, 0, stream, p);
-    else if (p.n_parts <= 8) hipLaunchKernelGGL((merge_states_kernel<F16, 8>), grid, block, 0, stream, p);
-    else if (p.n_parts <= 16) hipLaunchKernelGGL((merge_states_kernel<F16, 16>), grid, block, 0, stream, p);
-    else if (p.n_parts <= 32) hipLaunchKernelGGL((merge_states_kernel<F16, 32>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((merge_states_kernel<F16, 0>), grid, block, 0, stream, p);
+void launch_merge(const MergeParams &p, bool wide, dim3 grid, dim3 block, hipStream_t stream) {
+    if (wide && p.n_parts <= 4) hipLaunchKernelGGL((merge_states_kernel<F16, 4, 2>), grid, block, 0, stream, p);
+    else if (wide) hipLaunchKernelGGL((merge_states_kernel<F16, 8, 2>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 4) hipLaunchKernelGGL((merge_states_kernel<F16, 4, 1>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 8) hipLaunchKernelGGL((merge_states_kernel<F16, 8, 1>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 16) hipLaunchKernelGGL((merge_states_kernel<F16, 16, 1>), grid, block, 0, stream, p);
+    else if (p.n_parts <= 32) hipLaunchKernelGGL((merge_states_kernel<F16, 32, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_states_kernel<F16, 0, 1>), grid, block, 0, stream, p);
 }
 
 hipError_t launch_merge_states(const MergeParams &p, hipStream_t stream) {
     if (p.n_states == 0) return hipSuccess;
-    const int64_t tasks = p.n_states * ((p.dim + kMergeSeg - 1) / kMergeSeg);
+    const bool wide = p.n_parts <= 8 && p.n_states * ((p.dim + kMergeSeg - 1) / kMergeSeg) >= kWideMergeTasks;
+    const int seg = kMergeSeg * (wide ? 2 : 1);
+    const int64_t tasks = p.n_states * ((p.dim + seg - 1) / seg);
     const dim3 grid((unsigned)std::min<int64_t>((tasks + kMergeWaves - 1) / kMergeWaves, 1 << 20)),
         block(64 * kMergeWaves);
-    if (p.part_o_h) launch_merge<true>(p, grid, block, stream);
-    else launch_merge<false>(p, grid, block, stream);
+    if (p.part_o_h) launch_merge<true>(p, wide, grid, block, stream);
+    else launch_merge<false>(p, wide, grid, block, stream);
     return hipGetLastError();
 }
 

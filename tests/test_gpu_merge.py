@@ -69,6 +69,24 @@ def test_merge_matches_oracle(n_parts, dim):
     _compare(out16, l16, o_ref16, lse_ref16)
 
 
+@pytest.mark.parametrize("n_parts", [1, 4, 5, 8])
+@pytest.mark.parametrize("n_states,dim", [(2100, 260), (2048, 512), (900, 1028)])
+def test_merge_many_states_two_pieces_per_lane(n_parts, n_states, dim):
+    """At least 4096 tasks of 256 dims and at most 8 parts: each lane merges
+    two 4-dim pieces (512 dims per wavefront), including the tails of dims
+    that are not a multiple of 8."""
+    o, lse = _parts(n_parts, n_states, dim, seed=7300 + 17 * n_parts + dim)
+    o_ref, lse_ref = oracle.merge_states(o.astype(np.float64), lse.astype(np.float64))
+    out, l = kv4.merge_states(torch.from_numpy(o).to(DEV), torch.from_numpy(lse).to(DEV))
+    torch.cuda.synchronize()
+    _compare(out, l, o_ref, lse_ref)
+    o16 = o.astype(np.float16)
+    o_ref16, lse_ref16 = oracle.merge_states(o16.astype(np.float64), lse.astype(np.float64))
+    out16, l16 = kv4.merge_states(torch.from_numpy(o16).to(DEV), torch.from_numpy(lse).to(DEV))
+    torch.cuda.synchronize()
+    _compare(out16, l16, o_ref16, lse_ref16)
+
+
 def test_merge_into_strided_output_rows():
     """States written into rows of a wider output (out_state_stride > dim)."""
     n_parts, n_states, dim = 5, 64, 512
