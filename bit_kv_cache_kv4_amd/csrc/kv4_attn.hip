@@ -1522,8 +1522,9 @@ hipError_t launch_gather_dequant(const AttnParams &p, uint16_t *out, int32_t *sl
 // ln W; all parts empty gives o = 0, lse = -inf.
 constexpr int kMergeSeg = 256;                 // dims per wavefront and piece per lane
 constexpr int kMergeWaves = 4;                 // wavefronts per workgroup
-// at least this many 256-dim tasks (16 wavefronts per CU) and at most 8 parts:
-// 512 dims per wavefront.  Measured: the long-context decode step's merge
+// at least this many 256-dim tasks (16 wavefronts per CU), at most 8 parts, dim
+// a multiple of 8 and 16-byte aligned parts: 512 dims per wavefront, fp16
+// parts read 16 bytes a lane and part.  Measured: the long-context decode step's merge
 // (4096 states, 4 parts) 0.4 us faster; 8 requests x 64 heads with 16 parts
 // (1024 tasks) 1 us slower.
 constexpr int64_t kWideMergeTasks = 4096;
@@ -1568,9 +1569,16 @@ __device__ __forceinline__ void merge_task(const MergeParams &p, int64_t task, i
     PartPiece<F16> v[B > 0 ? B : 1][W];
     if constexpr (B > 0) {
 #pragma unroll
-        for (int s = 0; s < B; ++s)
+        for (int s = 0; s < B; ++s) {
+            if constexpr (W == 2 && F16) {     // dim % 8 == 0 and 16-byte aligned parts (checked at launch)
+                const half8_t x = *reinterpret_cast<const half8_t *>(p.part_o_h + o_t[0] + min(s, S - 1) * o_stride);
+                v[s][0] = half4_t{x[0], x[1], x[2], x[3]};
+                v[s][1] = half4_t{x[4], x[5], x[6], x[7]};
+            } else {
 #pragma unroll
-            for (int j = 0; j < W; ++j) v[s][j] = load_piece<F16>(p, o_t[j] + min(s, S - 1) * o_stride);
+                for (int j = 0; j < W; ++j) v[s][j] = load_piece<F16>(p, o_t[j] + min(s, S - 1) * o_stride);
+            }
+        }
     }
     const float my = lane < S ? my_raw : -__builtin_inff();
     auto lane_val = [](float x, int s) {
@@ -1656,7 +1664,9 @@ void launch_merge(const MergeParams &p, bool wide, dim3 grid, dim3 block, hipStr
 
 hipError_t launch_merge_states(const MergeParams &p, hipStream_t stream) {
     if (p.n_states == 0) return hipSuccess;
-    const bool wide = p.n_parts <= 8 && p.n_states * ((p.dim + kMergeSeg - 1) / kMergeSeg) >= kWideMergeTasks;
+    const bool aligned = !p.part_o_h || reinterpret_cast<uintptr_t>(p.part_o_h) % 16 == 0;
+    const bool wide = p.n_parts <= 8 && p.dim % 8 == 0 && aligned &&
+                      p.n_states * ((p.dim + kMergeSeg - 1) / kMergeSeg) >= kWideMergeTasks;
     const int seg = kMergeSeg * (wide ? 2 : 1);
     const int64_t tasks = p.n_states * ((p.dim + seg - 1) / seg);
     const dim3 grid((unsigned)std::min<int64_t>((tasks + kMergeWaves - 1) / kMergeWaves, 1 << 20)),

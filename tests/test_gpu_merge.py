@@ -70,11 +70,12 @@ def test_merge_matches_oracle(n_parts, dim):
 
 
 @pytest.mark.parametrize("n_parts", [1, 4, 5, 8])
-@pytest.mark.parametrize("n_states,dim", [(2100, 260), (2048, 512), (900, 1028)])
+@pytest.mark.parametrize("n_states,dim", [(2100, 264), (2048, 512), (900, 1032), (1100, 1028)])
 def test_merge_many_states_two_pieces_per_lane(n_parts, n_states, dim):
     """At least 4096 tasks of 256 dims and at most 8 parts: each lane merges
-    two 4-dim pieces (512 dims per wavefront), including the tails of dims
-    that are not a multiple of 8."""
+    two 4-dim pieces (512 dims per wavefront) when dim is a multiple of 8,
+    including segments that end inside a wavefront; dim 1028 keeps one piece
+    per lane."""
     o, lse = _parts(n_parts, n_states, dim, seed=7300 + 17 * n_parts + dim)
     o_ref, lse_ref = oracle.merge_states(o.astype(np.float64), lse.astype(np.float64))
     out, l = kv4.merge_states(torch.from_numpy(o).to(DEV), torch.from_numpy(lse).to(DEV))
